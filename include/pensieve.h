@@ -1,0 +1,192 @@
+/*
+ * pensieve.h -- C ABI of libpensieve: generalized paged attention for gfx950.
+ *
+ * The operation: in a unified batch of requests, every new query row of a
+ * request attends to that request's cached conversation K/V plus, causally,
+ * to the request's own new rows.  The K/V lives in fixed-size blocks of a
+ * shared pool, found through a per-request block table, so one request's KV
+ * is spread over non-contiguous memory ("Stateful Large Language Model
+ * Serving with Pensieve", Abstract and Methodology: the PagedAttention kernel
+ * generalised to several input tokens over a non-contiguous GPU cache;
+ * "LLM上下文缓存与状态复用机制的分析和探索", section 3.1: fixed-size blocks
+ * allocated on demand in non-contiguous memory).  Prefill requests, decode
+ * requests (one new row) and recompute rows (history tokens whose cache was
+ * dropped, recomputed ahead of the new rows -- Pensieve, Methodology) all run
+ * in one call.  Long contexts may be split into partitions whose partial
+ * results are merged ("PersistentKV: Page-Aware Decode Scheduling for
+ * Long-Context LLM Serving on Commodity GPUs", section 2, the split strategy).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All data pointers are DEVICE pointers unless the name ends in _host.
+ *   The caller allocates and owns every buffer; the library keeps no pointer
+ *   after a call returns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   device work is enqueued on it asynchronously; a call returns before the
+ *   GPU finishes.  Host arrays (_host) are fully read before the call returns.
+ * - Element type of Q, O and both pools: pensieve_dtype (F32, F16, BF16).
+ *   Arithmetic: dot products, softmax and accumulation in fp32; on F16/BF16
+ *   the softmax weights are rounded to the input type before the P.V product;
+ *   outputs are rounded to nearest-even.
+ * - block_size must be 16; head_dim must be 64 or 128; num_heads must be a
+ *   multiple of num_kv_heads.  Query head h reads KV head
+ *   h / (num_heads / num_kv_heads).
+ * - Layouts (row-major):
+ *     q, o          [total_q][num_heads][head_dim]; rows of request r are
+ *                   cu_q_lens[r] .. cu_q_lens[r+1]-1
+ *     k_pool        [num_blocks][num_kv_heads][16][head_dim]   (token rows)
+ *     v_pool        [num_blocks][num_kv_heads][head_dim][16]   (dim rows)
+ *     block_tables  [num_reqs][block_table_stride] int32: logical block j
+ *                   of request r lives in physical block block_tables[r][j]
+ *   Position t of request r is stored at offset t % 16 of physical block
+ *   block_tables[r][t / 16]; its slot is that block * 16 + t % 16.
+ * - context_lens[r] counts every KV position of request r resident after the
+ *   append of this step (history + recomputed + new).  A row at position p
+ *   sees keys 0..p.  Slots at positions >= context_lens[r], unused blocks and
+ *   block-table entries past ceil(context_lens[r]/16) may hold any bits, NaN
+ *   included; the output does not depend on them and they are never read.
+ * - Errors: every call returns a status.  Problems visible on the host
+ *   (null pointers, bad sizes, inconsistent host lengths, too small a
+ *   workspace) return INVALID_ARG / UNSUPPORTED / WORKSPACE_TOO_SMALL before
+ *   anything is enqueued.  A failed HIP call returns ERR_HIP.
+ *   pensieve_last_error() then describes the failure (per thread).
+ *   The contents of device arrays are the caller's contract: slots and block
+ *   ids in range, no duplicate slot in one append, query positions strictly
+ *   increasing within a request and below its context length.
+ */
+#ifndef PENSIEVE_H
+#define PENSIEVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pensieve_status {
+  PENSIEVE_OK = 0,
+  PENSIEVE_ERR_INVALID_ARG = 1,
+  PENSIEVE_ERR_UNSUPPORTED = 2,
+  PENSIEVE_ERR_WORKSPACE_TOO_SMALL = 3,
+  PENSIEVE_ERR_HIP = 4
+} pensieve_status;
+
+typedef enum pensieve_dtype { PENSIEVE_F32 = 0, PENSIEVE_F16 = 1, PENSIEVE_BF16 = 2 } pensieve_dtype;
+
+/* pensieve_batch_desc.flags: route every work item to the vector-ALU kernel
+ * (the matrix-core kernel is otherwise used for items with many query rows
+ * on F16/BF16).  Results agree within the stated tolerances either way. */
+#define PENSIEVE_FLAG_VECTOR_ONLY 1
+
+/* Shape of one unified batch plus host copies of its lengths (used to
+ * validate and to plan the work; the device copies passed to the compute
+ * calls must hold the same values). */
+typedef struct pensieve_batch_desc {
+  int32_t num_reqs;
+  int32_t num_heads;            /* query heads Hq */
+  int32_t num_kv_heads;         /* KV heads Hkv; divides Hq */
+  int32_t head_dim;             /* 64 or 128 */
+  int32_t block_size;           /* 16 */
+  int32_t num_blocks;           /* blocks in each pool */
+  int32_t block_table_stride;   /* int32 entries per block-table row */
+  int32_t dtype;                /* pensieve_dtype */
+  float softmax_scale;          /* scale on q.k before the softmax, e.g. 1/sqrt(head_dim); > 0 */
+  int32_t flags;                /* 0, or PENSIEVE_FLAG_VECTOR_ONLY */
+  const int32_t* context_lens_host;  /* [num_reqs] */
+  const int32_t* cu_q_lens_host;     /* [num_reqs + 1], cu_q_lens_host[0] == 0 */
+} pensieve_batch_desc;
+
+/* Library version string, e.g. "pensieve 0.1 gfx950". */
+const char* pensieve_version(void);
+
+/* Text of the last failure on the calling thread ("" after success). */
+const char* pensieve_last_error(void);
+
+/*
+ * KV append: for every token t in [0, num_tokens) with slot_mapping[t] >= 0,
+ * write k_new[t] into k_pool at block slot/16, offset slot%16 (a [Hkv][d]
+ * row set) and v_new[t] into v_pool at the same place (column slot%16 of the
+ * block's [d][16] tiles).  A negative slot skips the token.  The copy is
+ * bit-exact; nothing else in the pools changes.
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim], dtype elements
+ *   slot_mapping  [num_tokens] int32, each < num_blocks*16, no duplicates
+ * Follows the block-pool contract of the blog post cited above (section
+ * 3.1): new tokens land in whatever block the caller allocated.
+ */
+pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                   const int32_t* slot_mapping, int32_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * Workspace needed by pensieve_attn_fwd (num_partitions == 0) or by
+ * pensieve_attn_split_partial (num_partitions >= 1) for this batch.  The
+ * workspace holds the device copy of the work list; it is plain device
+ * memory owned by the caller, needs no initialisation and may be reused by
+ * the next call on the same stream.
+ */
+pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, int32_t num_partitions,
+                                             size_t* bytes);
+
+/*
+ * Generalized paged attention (Pensieve, Abstract/Methodology):
+ *   o[i][h][:] = sum_t softmax_t(scale * q[i][h].K[t]) V[t],  t <= pos(i),
+ * over the KV of row i's request, head h / (Hq/Hkv).
+ *   q_pos  [total_q] int32 absolute position of every row, or NULL: row j of
+ *          request r (0-based) then sits at context_lens[r] - q_r + j.
+ * o must not alias q.  Run the pensieve_kv_append of this step's rows first,
+ * on the same stream.
+ */
+pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, const int32_t* cu_q_lens,
+                                  const int32_t* q_pos, void* o, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * Split-KV partials (PersistentKV, section 2: one long context cut into
+ * partitions processed in parallel).  Request r's logical blocks are cut
+ * into num_partitions ranges of S = ceil(ceil(L_r/16)/num_partitions)
+ * blocks: partition k covers positions [16kS, 16(k+1)S) clipped to [0, L_r).
+ * For row i, head h, partition k (index (i*Hq + h)*P + k):
+ *   part_m[.] = max scaled score over the visible keys of the partition
+ *   part_l[.] = sum of exp(score - part_m) over them
+ *   part_o[.][:] = that weighted sum of V divided by part_l (fp32)
+ * A partition with no visible key stores m = -inf, l = 0, o = 0.
+ *   part_o [total_q][Hq][P][head_dim] fp32, part_m/part_l [total_q][Hq][P] fp32
+ */
+pensieve_status pensieve_attn_split_partial(const pensieve_batch_desc* desc, int32_t num_partitions,
+                                            const void* q, const void* k_pool, const void* v_pool,
+                                            const int32_t* block_tables, const int32_t* context_lens,
+                                            const int32_t* cu_q_lens, const int32_t* q_pos,
+                                            float* part_o, float* part_m, float* part_l,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge of split partials: M = max_k m_k, w_k = l_k exp(m_k - M),
+ * o = sum_k w_k o_k / sum_k w_k (partitions with l_k = 0 weigh nothing),
+ * rounded to dtype.  Shapes as in pensieve_attn_split_partial; o is
+ * [total_q][num_heads][head_dim].
+ */
+pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part_m, const float* part_l,
+                                          int32_t total_q, int32_t num_heads, int32_t head_dim,
+                                          int32_t num_partitions, int32_t dtype, void* o, void* stream);
+
+/*
+ * Host-only introspection of the work list pensieve_attn_fwd
+ * (num_partitions == 0) or pensieve_attn_split_partial would build for this
+ * batch.  Writes up to max_items records of 8 int32 each:
+ *   {kernel, request, kv_head, first row in request, rows, partition,
+ *    partitions, estimated cost}
+ * with kernel 0 = vector path, 1 = matrix-core path, and sets *num_items to
+ * the full count.  No GPU is touched.
+ */
+pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num_partitions,
+                                    int32_t* items_host, int32_t max_items, int32_t* num_items);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PENSIEVE_H */

@@ -1,0 +1,25 @@
+"""paged_kv_token_amd: generalized paged attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libpensieve.so`` (HIP kernels behind the C ABI of
+``include/pensieve.h``); this package holds its sources, the build script
+and a thin ctypes binding with the same entry-point names.
+"""
+
+from .binding import (  # noqa: F401
+    BatchDesc,
+    PensieveError,
+    PENSIEVE_BF16,
+    PENSIEVE_F16,
+    PENSIEVE_F32,
+    PENSIEVE_FLAG_VECTOR_ONLY,
+    dtype_code,
+    load_library,
+    make_desc,
+    pensieve_attn_fwd,
+    pensieve_attn_split_merge,
+    pensieve_attn_split_partial,
+    pensieve_attn_workspace_size,
+    pensieve_debug_plan,
+    pensieve_kv_append,
+    pensieve_version,
+)

@@ -1,0 +1,202 @@
+"""Thin ctypes binding of libpensieve (include/pensieve.h).
+
+Argument marshalling only: every function takes torch tensors for device
+buffers (PyTorch supplies device memory and streams), checks that they are
+contiguous tensors of the expected dtype on the current GPU, and calls the C
+entry point of the same name.  All arithmetic happens in the library's HIP
+kernels; there is no fallback path.  A missing library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpensieve.so")
+
+PENSIEVE_OK = 0
+PENSIEVE_ERR_INVALID_ARG = 1
+PENSIEVE_ERR_UNSUPPORTED = 2
+PENSIEVE_ERR_WORKSPACE_TOO_SMALL = 3
+PENSIEVE_ERR_HIP = 4
+PENSIEVE_F32, PENSIEVE_F16, PENSIEVE_BF16 = 0, 1, 2
+PENSIEVE_FLAG_VECTOR_ONLY = 1
+
+EXPORTED = (
+    "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",
+    "pensieve_attn_fwd", "pensieve_attn_split_partial", "pensieve_attn_split_merge", "pensieve_debug_plan",
+)
+
+
+class PensieveError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pensieve status {status}: {message}")
+        self.status = status
+
+
+class BatchDesc(ctypes.Structure):
+    """Mirror of pensieve_batch_desc; keeps its host length arrays alive."""
+
+    _fields_ = [
+        ("num_reqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("block_table_stride", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("flags", ctypes.c_int32),
+        ("context_lens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("cu_q_lens_host", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libpensieve.so (built in-tree by paged_kv_token_amd.build)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m paged_kv_token_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i32p = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+    dp = ctypes.POINTER(BatchDesc)
+    lib.pensieve_version.restype = ctypes.c_char_p
+    lib.pensieve_last_error.restype = ctypes.c_char_p
+    lib.pensieve_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pensieve_attn_workspace_size.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.pensieve_attn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.pensieve_attn_split_partial.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.c_size_t, vp]
+    lib.pensieve_attn_split_merge.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.pensieve_debug_plan.argtypes = [dp, i32, i32p, i32, i32p]
+    for name in EXPORTED[2:]:
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != PENSIEVE_OK:
+        raise PensieveError(status, load_library().pensieve_last_error().decode())
+
+
+# ---- tensor marshalling ------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: PENSIEVE_F32, torch.float16: PENSIEVE_F16, torch.bfloat16: PENSIEVE_BF16}[t.dtype]
+
+
+def _ptr(t, name: str, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(*, num_heads: int, num_kv_heads: int, head_dim: int, num_blocks: int, block_table_stride: int,
+              dtype: int, softmax_scale: float, context_lens_host, cu_q_lens_host, block_size: int = 16,
+              flags: int = 0) -> BatchDesc:
+    ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_q_lens_host, dtype=np.int32)
+    d = BatchDesc(len(ctx), num_heads, num_kv_heads, head_dim, block_size, num_blocks, block_table_stride, dtype,
+                  float(softmax_scale), flags,
+                  ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                  cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    d._keep = (ctx, cu)  # host arrays must outlive the descriptor
+    return d
+
+
+# ---- entry points --------------------------------------------------------------------
+def pensieve_version() -> str:
+    return load_library().pensieve_version().decode()
+
+
+def pensieve_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None):
+    torch = _torch()
+    lib = load_library()
+    n, hkv, d = k_new.shape
+    nb = k_pool.shape[0]
+    _check(lib.pensieve_kv_append(_ptr(k_new, "k_new"), _ptr(v_new, "v_new", k_new.dtype),
+                                  _ptr(k_pool, "k_pool", k_new.dtype), _ptr(v_pool, "v_pool", k_new.dtype),
+                                  _ptr(slot_mapping, "slot_mapping", torch.int32), n, hkv, d, k_pool.shape[2], nb,
+                                  dtype_code(k_new), _stream(stream)))
+
+
+def pensieve_attn_workspace_size(desc: BatchDesc, num_partitions: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().pensieve_attn_workspace_size(ctypes.byref(desc), num_partitions, ctypes.byref(out)))
+    return int(out.value)
+
+
+def pensieve_attn_fwd(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos, o,
+                      workspace, stream=None):
+    torch = _torch()
+    _check(load_library().pensieve_attn_fwd(
+        ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
+        _ptr(block_tables, "block_tables", torch.int32), _ptr(context_lens, "context_lens", torch.int32),
+        _ptr(cu_q_lens, "cu_q_lens", torch.int32), _ptr(q_pos, "q_pos", torch.int32), _ptr(o, "o", q.dtype),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def pensieve_attn_split_partial(desc: BatchDesc, num_partitions: int, q, k_pool, v_pool, block_tables,
+                                context_lens, cu_q_lens, q_pos, part_o, part_m, part_l, workspace, stream=None):
+    torch = _torch()
+    _check(load_library().pensieve_attn_split_partial(
+        ctypes.byref(desc), num_partitions, _ptr(q, "q"), _ptr(k_pool, "k_pool", q.dtype),
+        _ptr(v_pool, "v_pool", q.dtype), _ptr(block_tables, "block_tables", torch.int32),
+        _ptr(context_lens, "context_lens", torch.int32), _ptr(cu_q_lens, "cu_q_lens", torch.int32),
+        _ptr(q_pos, "q_pos", torch.int32), _ptr(part_o, "part_o", torch.float32),
+        _ptr(part_m, "part_m", torch.float32), _ptr(part_l, "part_l", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def pensieve_attn_split_merge(part_o, part_m, part_l, o, stream=None):
+    torch = _torch()
+    t, hq, p, d = part_o.shape
+    _check(load_library().pensieve_attn_split_merge(
+        _ptr(part_o, "part_o", torch.float32), _ptr(part_m, "part_m", torch.float32),
+        _ptr(part_l, "part_l", torch.float32), t, hq, d, p, dtype_code(o), _ptr(o, "o"), _stream(stream)))
+
+
+def pensieve_debug_plan(desc: BatchDesc, num_partitions: int = 0) -> np.ndarray:
+    """Work list the library would launch: int32 [n][8] (see pensieve.h)."""
+    lib = load_library()
+    n = ctypes.c_int32(0)
+    _check(lib.pensieve_debug_plan(ctypes.byref(desc), num_partitions, None, 0, ctypes.byref(n)))
+    out = np.zeros((max(n.value, 1), 8), dtype=np.int32)
+    _check(lib.pensieve_debug_plan(ctypes.byref(desc), num_partitions,
+                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n)))
+    return out[:n.value]

@@ -1,0 +1,430 @@
+// C ABI of libpensieve: argument checks, the host work planner, pinned
+// staging of the work list, and kernel launches on the caller's stream.
+//
+// Planning follows the compact work queue of "PersistentKV: Page-Aware
+// Decode Scheduling for Long-Context LLM Serving on Commodity GPUs"
+// (section 2): the unified batch becomes a dense list of real work items
+// (request, KV head, row range, KV partition) with no padding items, ordered
+// longest first so the hardware dispatcher balances the tail.  Items with
+// many query vectors go to the matrix-core kernel; decode rows and small row
+// groups go to the vector kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "launch.h"
+#include "pensieve.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pensieve_status fail(pensieve_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pensieve_status ok() {
+  g_last_error.clear();
+  return PENSIEVE_OK;
+}
+
+pensieve_status hip_fail(hipError_t e, const char* what) {
+  return fail(PENSIEVE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kBlockSize = 16;
+constexpr int kVectorRowsMax = 8;    // query vectors per vector-kernel item
+constexpr int kMfmaRows = 128;       // query vectors per matrix-core item
+constexpr int kMaxPartitions = 256;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int dtype) { return dtype == PENSIEVE_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == PENSIEVE_F32 || dtype == PENSIEVE_F16 || dtype == PENSIEVE_BF16; }
+
+int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+pensieve_status check_desc(const pensieve_batch_desc* d) {
+  if (!d) return fail(PENSIEVE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_reqs < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_reqs < 0");
+  if (d->num_heads <= 0 || d->num_kv_heads <= 0)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "num_heads and num_kv_heads must be > 0");
+  if (d->num_heads % d->num_kv_heads != 0)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "num_heads (%d) is not a multiple of num_kv_heads (%d)", d->num_heads,
+                d->num_kv_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
+  if (d->block_size != kBlockSize) return fail(PENSIEVE_ERR_UNSUPPORTED, "block_size %d unsupported (16)", d->block_size);
+  if (!valid_dtype(d->dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->num_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_blocks must be > 0");
+  if (d->block_table_stride <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "block_table_stride must be > 0");
+  if (!(d->softmax_scale > 0.f)) return fail(PENSIEVE_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  if (d->flags & ~PENSIEVE_FLAG_VECTOR_ONLY) return fail(PENSIEVE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (d->num_reqs > 0 && (!d->context_lens_host || !d->cu_q_lens_host))
+    return fail(PENSIEVE_ERR_INVALID_ARG, "context_lens_host / cu_q_lens_host is NULL");
+  if (d->num_reqs > 0 && d->cu_q_lens_host[0] != 0) return fail(PENSIEVE_ERR_INVALID_ARG, "cu_q_lens_host[0] != 0");
+  for (int r = 0; r < d->num_reqs; ++r) {
+    const int L = d->context_lens_host[r];
+    const long q = (long)d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+    if (L < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "context_lens[%d] = %d < 0", r, L);
+    if (q < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "cu_q_lens decreases at request %d", r);
+    if (q > L) return fail(PENSIEVE_ERR_INVALID_ARG, "request %d has %ld query rows but context length %d", r, q, L);
+    const long nblk = ((long)L + kBlockSize - 1) / kBlockSize;
+    if (nblk > d->block_table_stride)
+      return fail(PENSIEVE_ERR_INVALID_ARG, "request %d needs %ld blocks but block_table_stride is %d", r, nblk,
+                  d->block_table_stride);
+    if (nblk > (long)d->num_blocks)
+      return fail(PENSIEVE_ERR_INVALID_ARG, "request %d needs %ld blocks but the pool has %d", r, nblk, d->num_blocks);
+  }
+  return PENSIEVE_OK;
+}
+
+// ---- planning -------------------------------------------------------------------------
+enum Kernel { kVector = 0, kMatrix = 1 };
+
+struct PlannedItem {
+  pk::WorkItem w;
+  int kernel;
+  int param;        // vector: query vectors per item (1,2,4,8); matrix: group size
+  long long cost;
+};
+
+struct Segment {
+  int kernel;
+  int param;
+  int begin;
+  int count;
+};
+
+struct Plan {
+  std::vector<pk::WorkItem> items;
+  std::vector<PlannedItem> planned;   // same order as items
+  std::vector<Segment> segments;
+  size_t bytes() const { return align_up(items.size() * sizeof(pk::WorkItem)); }
+};
+
+bool matrix_ok(const pensieve_batch_desc* d) {
+  const int G = d->num_heads / d->num_kv_heads;
+  if (d->dtype == PENSIEVE_F32 || (d->flags & PENSIEVE_FLAG_VECTOR_ONLY)) return false;
+  return G >= 1 && G <= 32 && (32 % G) == 0;
+}
+
+void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
+  const int G = d->num_heads / d->num_kv_heads;
+  const bool mat = matrix_ok(d);
+  const int P = num_partitions >= 1 ? num_partitions : 1;
+  std::vector<PlannedItem> all;
+  for (int r = 0; r < d->num_reqs; ++r) {
+    const int L = d->context_lens_host[r];
+    const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+    if (q == 0) continue;
+    const long long nblk = (L + kBlockSize - 1) / kBlockSize;
+    const long long per = (nblk + P - 1) / P;
+    const bool use_matrix = mat && (long long)q * G > kVectorRowsMax;
+    for (int part = 0; part < P; ++part) {
+      const long long blocks = std::max(0LL, std::min(per, nblk - part * per));
+      for (int g = 0; g < d->num_kv_heads; ++g) {
+        if (use_matrix) {
+          const int tok_tile = kMfmaRows / G;
+          for (int q0 = 0; q0 < q; q0 += tok_tile) {
+            PlannedItem p{};
+            p.w = {r, q0, std::min(tok_tile, q - q0), g, 0, G, part, P};
+            p.kernel = kMatrix;
+            p.param = G;
+            p.cost = (blocks + 1) * 64;
+            all.push_back(p);
+          }
+        } else {
+          const int heads_per = std::min(G, kVectorRowsMax);
+          const int tok_per = std::max(1, kVectorRowsMax / heads_per);
+          for (int h0 = 0; h0 < G; h0 += heads_per) {
+            const int hc = std::min(heads_per, G - h0);
+            for (int q0 = 0; q0 < q; q0 += tok_per) {
+              const int qc = std::min(tok_per, q - q0);
+              PlannedItem p{};
+              p.w = {r, q0, qc, g, h0, hc, part, P};
+              p.kernel = kVector;
+              p.param = next_pow2(qc * hc);
+              p.cost = (blocks + 1) * (4 + qc * hc);
+              all.push_back(p);
+            }
+          }
+        }
+      }
+    }
+  }
+  // Segments: matrix items first, then vector items by width; longest first inside each.
+  auto key = [](const PlannedItem& p) { return p.kernel == kMatrix ? 0 : p.param; };
+  std::stable_sort(all.begin(), all.end(), [&](const PlannedItem& a, const PlannedItem& b) {
+    if (key(a) != key(b)) return key(a) < key(b);
+    return a.cost > b.cost;
+  });
+  plan.items.clear();
+  plan.segments.clear();
+  plan.planned = all;
+  for (size_t i = 0; i < all.size(); ++i) {
+    plan.items.push_back(all[i].w);
+    if (plan.segments.empty() || plan.segments.back().kernel != all[i].kernel ||
+        plan.segments.back().param != all[i].param) {
+      plan.segments.push_back({all[i].kernel, all[i].param, (int)i, 0});
+    }
+    plan.segments.back().count++;
+  }
+}
+
+// ---- pinned staging of work lists ---------------------------------------------------------
+// Each device gets a small ring of page-locked host buffers; a work list is
+// copied into the next one and sent with hipMemcpyAsync on the caller's
+// stream.  An event per buffer guards its reuse until the copy has finished.
+struct Stager {
+  static constexpr int kSlots = 8;
+  struct Slot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  std::mutex mu;
+  Slot slots[kSlots];
+  int next = 0;
+};
+
+std::mutex g_stagers_mu;
+std::unordered_map<int, Stager*> g_stagers;
+
+Stager* stager_for_current_device(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_stagers_mu);
+  auto it = g_stagers.find(dev);
+  if (it != g_stagers.end()) return it->second;
+  Stager* s = new Stager();
+  g_stagers[dev] = s;
+  return s;
+}
+
+hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  hipError_t e;
+  Stager* st = stager_for_current_device(&e);
+  if (!st) return e;
+  std::lock_guard<std::mutex> lk(st->mu);
+  Stager::Slot& s = st->slots[st->next];
+  st->next = (st->next + 1) % Stager::kSlots;
+  if (s.pending) {
+    if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return e;
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host && (e = hipHostFree(s.host)) != hipSuccess) return e;
+    s.host = nullptr;
+    size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    if ((e = hipHostMalloc(&s.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
+    s.cap = cap;
+  }
+  if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
+  std::memcpy(s.host, src, bytes);
+  if ((e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess) return e;
+  if ((e = hipEventRecord(s.ev, stream)) != hipSuccess) return e;
+  s.pending = true;
+  return hipSuccess;
+}
+
+pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::AttnArgs& args, void* workspace,
+                         hipStream_t stream) {
+  hipError_t e = stage_to_device(workspace, plan.items.data(), plan.items.size() * sizeof(pk::WorkItem), stream);
+  if (e != hipSuccess) return hip_fail(e, "work-list upload");
+  const pk::WorkItem* dev_items = static_cast<const pk::WorkItem*>(workspace);
+  for (const Segment& s : plan.segments) {
+    pk::AttnArgs a = args;
+    a.items = dev_items + s.begin;
+    a.num_items = s.count;
+    if (s.kernel == kMatrix)
+      e = pk::launch_attn_mfma(a, d->dtype, d->head_dim, s.param, stream);
+    else
+      e = pk::launch_attn_vector(a, d->dtype, d->head_dim, s.param, stream);
+    if (e != hipSuccess) return hip_fail(e, s.kernel == kMatrix ? "matrix-core attention launch" : "vector attention launch");
+  }
+  return ok();
+}
+
+pk::AttnArgs make_args(const pensieve_batch_desc* d, const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* bt, const int32_t* ctx, const int32_t* cu, const int32_t* q_pos) {
+  pk::AttnArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.k_pool = static_cast<const uint8_t*>(k_pool);
+  a.v_pool = static_cast<const uint8_t*>(v_pool);
+  a.block_tables = bt;
+  a.context_lens = ctx;
+  a.cu_q_lens = cu;
+  a.q_pos = q_pos;
+  a.num_heads = d->num_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.bt_stride = d->block_table_stride;
+  a.scale = d->softmax_scale;
+  a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  return a;
+}
+
+int total_q(const pensieve_batch_desc* d) { return d->num_reqs > 0 ? d->cu_q_lens_host[d->num_reqs] : 0; }
+
+pensieve_status check_attn_pointers(const pensieve_batch_desc* d, const void* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* bt, const int32_t* ctx, const int32_t* cu) {
+  if (total_q(d) == 0) return PENSIEVE_OK;
+  if (!q || !k_pool || !v_pool || !bt || !ctx || !cu)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "a device pointer (q, pools, block_tables, context_lens, cu_q_lens) is NULL");
+  return PENSIEVE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pensieve_version(void) { return "pensieve 0.1 gfx950"; }
+
+const char* pensieve_last_error(void) { return g_last_error.c_str(); }
+
+pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                   const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                                   void* stream) {
+  if (num_tokens < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_kv_heads <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+  if (head_dim != 64 && head_dim != 128) return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported", head_dim);
+  if (block_size != kBlockSize) return fail(PENSIEVE_ERR_UNSUPPORTED, "block_size %d unsupported", block_size);
+  if (!valid_dtype(dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (num_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_blocks must be > 0");
+  if (num_kv_heads > 65535) return fail(PENSIEVE_ERR_UNSUPPORTED, "num_kv_heads > 65535");
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "a device pointer is NULL");
+  hipError_t e = pk::launch_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                      elem_bytes(dtype), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return ok();
+}
+
+pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, int32_t num_partitions, size_t* bytes) {
+  pensieve_status s = check_desc(desc);
+  if (s != PENSIEVE_OK) return s;
+  if (!bytes) return fail(PENSIEVE_ERR_INVALID_ARG, "bytes is NULL");
+  if (num_partitions < 0 || num_partitions > kMaxPartitions)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "num_partitions must be in [0, %d]", kMaxPartitions);
+  Plan plan;
+  build_plan(desc, num_partitions, plan);
+  *bytes = plan.bytes();
+  return ok();
+}
+
+pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* cu_q_lens, const int32_t* q_pos, void* o, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pensieve_status s = check_desc(desc);
+  if (s != PENSIEVE_OK) return s;
+  if ((s = check_attn_pointers(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens)) != PENSIEVE_OK) return s;
+  if (total_q(desc) == 0) return ok();
+  if (!o) return fail(PENSIEVE_ERR_INVALID_ARG, "o is NULL");
+  if (o == q) return fail(PENSIEVE_ERR_INVALID_ARG, "o must not alias q");
+  Plan plan;
+  build_plan(desc, 0, plan);
+  if (!workspace || workspace_bytes < plan.bytes())
+    return fail(PENSIEVE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes(),
+                workspace ? workspace_bytes : (size_t)0);
+  pk::AttnArgs a = make_args(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos);
+  a.o = static_cast<uint8_t*>(o);
+  a.write_partials = 0;
+  a.part_stride = 1;
+  return run_plan(desc, plan, a, workspace, static_cast<hipStream_t>(stream));
+}
+
+pensieve_status pensieve_attn_split_partial(const pensieve_batch_desc* desc, int32_t num_partitions, const void* q,
+                                            const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                            const int32_t* context_lens, const int32_t* cu_q_lens,
+                                            const int32_t* q_pos, float* part_o, float* part_m, float* part_l,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  pensieve_status s = check_desc(desc);
+  if (s != PENSIEVE_OK) return s;
+  if (num_partitions < 1 || num_partitions > kMaxPartitions)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "num_partitions must be in [1, %d]", kMaxPartitions);
+  if ((s = check_attn_pointers(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens)) != PENSIEVE_OK) return s;
+  if (total_q(desc) == 0) return ok();
+  if (!part_o || !part_m || !part_l) return fail(PENSIEVE_ERR_INVALID_ARG, "a partial buffer is NULL");
+  Plan plan;
+  build_plan(desc, num_partitions, plan);
+  if (!workspace || workspace_bytes < plan.bytes())
+    return fail(PENSIEVE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes(),
+                workspace ? workspace_bytes : (size_t)0);
+  pk::AttnArgs a = make_args(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos);
+  a.part_o = part_o;
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_stride = num_partitions;
+  a.write_partials = 1;
+  return run_plan(desc, plan, a, workspace, static_cast<hipStream_t>(stream));
+}
+
+pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part_m, const float* part_l,
+                                          int32_t total_rows, int32_t num_heads, int32_t head_dim,
+                                          int32_t num_partitions, int32_t dtype, void* o, void* stream) {
+  if (total_rows < 0 || num_heads <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "bad total_q / num_heads");
+  if (head_dim != 64 && head_dim != 128) return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported", head_dim);
+  if (num_partitions < 1 || num_partitions > kMaxPartitions)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "num_partitions must be in [1, %d]", kMaxPartitions);
+  if (!valid_dtype(dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  const long long rows = (long long)total_rows * num_heads;
+  if (rows == 0) return ok();
+  if (rows > (1LL << 31) - 4) return fail(PENSIEVE_ERR_UNSUPPORTED, "too many rows");
+  if (!part_o || !part_m || !part_l || !o) return fail(PENSIEVE_ERR_INVALID_ARG, "a pointer is NULL");
+  hipError_t e = pk::launch_split_merge(part_o, part_m, part_l, (int)rows, head_dim, num_partitions, dtype, o,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "split merge launch");
+  return ok();
+}
+
+pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num_partitions, int32_t* items_host,
+                                    int32_t max_items, int32_t* num_items) {
+  pensieve_status s = check_desc(desc);
+  if (s != PENSIEVE_OK) return s;
+  if (num_partitions < 0 || num_partitions > kMaxPartitions)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "num_partitions must be in [0, %d]", kMaxPartitions);
+  if (!num_items || (max_items > 0 && !items_host)) return fail(PENSIEVE_ERR_INVALID_ARG, "NULL output");
+  Plan plan;
+  build_plan(desc, num_partitions, plan);
+  *num_items = (int32_t)plan.planned.size();
+  for (int i = 0; i < (int)plan.planned.size() && i < max_items; ++i) {
+    const PlannedItem& p = plan.planned[i];
+    int32_t* o = items_host + 8 * i;
+    o[0] = p.kernel;
+    o[1] = p.w.req;
+    o[2] = p.w.kv_head;
+    o[3] = p.w.q_begin;
+    o[4] = p.w.q_count;
+    o[5] = p.w.part;
+    o[6] = p.w.num_parts;
+    o[7] = (int32_t)std::min<long long>(p.cost, 0x7fffffff);
+  }
+  return ok();
+}
+
+}  // extern "C"

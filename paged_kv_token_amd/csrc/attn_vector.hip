@@ -1,0 +1,260 @@
+// Vector-ALU generalized paged attention for items with few query vectors.
+//
+// Serves decode rows (one new token), small groups of rows, and every fp32
+// batch.  One workgroup (4 waves) handles one work item: up to NQ query
+// vectors (tokens x query heads of one KV head) of one request, over one
+// partition of that request's KV blocks.  The four waves stride over the
+// item's blocks; each wave keeps an online softmax per query vector in
+// registers and the waves merge through LDS at the end.
+//
+// Per 16-token block a wave issues 16-byte loads that cover the K tile
+// [16][D] and the V tile [D][16] exactly once (64 lanes x 16 B per load), so
+// HBM traffic is the algorithmic K/V bytes.  K: lane l of load i holds dims
+// (l % LPT) * EPC .. +EPC of token i * TPI + l / LPT; the q.k partial sums
+// are reduced over the LPT lanes of a token with DPP row operations.  V: lane
+// l of load j holds tokens (l % CPR) * EPC .. +EPC of dim row j * DPI + l / CPR;
+// the softmax weights reach it through a small per-wave LDS array.
+//
+// Semantics ("Stateful Large Language Model Serving with Pensieve", Abstract:
+// attention of several new tokens over a non-contiguous cache): row i sees
+// keys at positions 0..pos(i) of its request; masked keys and slots past the
+// context length never enter the sums (scores are selected to -inf and V
+// elements past the context length are selected to 0, so stale NaN cannot
+// leak in).
+#include "device_common.h"
+#include "launch.h"
+
+namespace pk {
+
+template <int DT, int D, int NQ>
+__global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
+  constexpr int EB = DTypeInfo<DT>::bytes;
+  constexpr int EPC = 16 / EB;          // elements per 16-byte chunk
+  constexpr int LPT = D * EB / 16;      // lanes holding one K token row
+  constexpr int TPI = 64 / LPT;         // K tokens per load
+  constexpr int KI = 16 / TPI;          // K loads per block
+  constexpr int CPR = EB;               // 16-byte chunks per V dim row (16 tokens)
+  constexpr int DPI = 64 / CPR;         // V dim rows per load
+  constexpr int VI = D / DPI;           // V loads per block
+  constexpr int NW = 4;
+  constexpr size_t TILE = (size_t)16 * D * EB;
+  static_assert(LPT >= 1 && LPT <= 32, "unsupported row width");
+
+  __shared__ __attribute__((aligned(16))) float s_p[NW][NQ][16];
+  __shared__ float s_m[NW][NQ];
+  __shared__ float s_l[NW][NQ];
+  __shared__ float s_acc[NW][NQ][D];
+
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const WorkItem it = a.items[blockIdx.x];
+  const int r = it.req, g = it.kv_head;
+  const int Hq = a.num_heads, Hkv = a.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int L = a.context_lens[r];
+  const int row0 = a.cu_q_lens[r];
+  const int q_r = a.cu_q_lens[r + 1] - row0;
+  const int hc = it.head_count;
+  const int nrows = it.q_count * hc;
+  const float c = a.scale_log2;
+
+  // ---- query vectors and their positions -----------------------------------
+  float qv[NQ][EPC];
+  int qpos[NQ];
+  int pmin = 0x7fffffff, pmax = -1;
+  const int dim0 = (lane % LPT) * EPC;
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    const bool valid = n < nrows;
+    const int tok = valid ? n / hc : 0;
+    const int h = g * G + it.head_begin + (valid ? n % hc : 0);
+    const int row = row0 + it.q_begin + tok;
+    const u32x4 qw = *reinterpret_cast<const u32x4*>(a.q + (((size_t)row * Hq + h) * D + dim0) * EB);
+    unpack16<DT>(qw, qv[n]);
+    int p = -1;
+    if (valid) p = a.q_pos ? a.q_pos[row] : (L - q_r + it.q_begin + tok);
+    qpos[n] = p;
+    if (valid) { pmin = min(pmin, p); pmax = max(pmax, p); }
+  }
+
+  // ---- this item's block range ----------------------------------------------
+  const int nblk = (L + 15) >> 4;
+  const int per = (nblk + it.num_parts - 1) / it.num_parts;
+  const int kb0 = it.part * per;
+  const int kb1 = min(min(kb0 + per, nblk), (pmax >> 4) + 1);
+
+  float m[NQ], l[NQ], acc[NQ][VI];
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    m[n] = -INFINITY; l[n] = 0.f;
+#pragma unroll
+    for (int j = 0; j < VI; ++j) acc[n][j] = 0.f;
+  }
+
+  const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
+  auto load = [&](int blk, u32x4* kr, u32x4* vr) {
+    const int phys = bt[blk];
+    const uint8_t* kt = a.k_pool + ((size_t)phys * Hkv + g) * TILE;
+    const uint8_t* vt = a.v_pool + ((size_t)phys * Hkv + g) * TILE;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kt + (size_t)(i * 64 + lane) * 16);
+#pragma unroll
+    for (int j = 0; j < VI; ++j) vr[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)(j * 64 + lane) * 16);
+  };
+
+  auto process = [&](int blk, const u32x4* kr, const u32x4* vr) {
+    const int base = blk * 16;
+    const bool need_mask = base + 15 > pmin;
+    float sc[NQ][KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      float kf[EPC];
+      unpack16<DT>(kr[i], kf);
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s = fmaf(qv[n][e], kf[e], s);
+        sc[n][i] = group_sum<LPT>(s);
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const int t = base + i * TPI + lane / LPT;
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) sc[n][i] = (t <= qpos[n]) ? sc[n][i] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NQ; ++n) {
+      float bm = sc[n][0];
+#pragma unroll
+      for (int i = 1; i < KI; ++i) bm = fmaxf(bm, sc[n][i]);
+      bm = xor_max_from<LPT>(bm);
+      const float m_new = fmaxf(m[n], bm);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = fast_exp2((m[n] - m_use) * c);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        const float p = fast_exp2((sc[n][i] - m_use) * c);
+        ps += p;
+        if (lane % LPT == 0) s_p[w][n][i * TPI + lane / LPT] = p;
+      }
+      l[n] = l[n] * corr + ps;
+#pragma unroll
+      for (int j = 0; j < VI; ++j) acc[n][j] *= corr;
+      m[n] = m_new;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int tc = (lane % CPR) * EPC;      // first token of this lane's V chunk
+    const bool zero_tail = base + 16 > L;
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      float vf[EPC];
+      unpack16<DT>(vr[j], vf);
+      if (zero_tail) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vf[e] = (base + tc + e < L) ? vf[e] : 0.f;
+      }
+#pragma unroll
+      for (int n = 0; n < NQ; ++n) {
+        float s = acc[n][j];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) s = fmaf(s_p[w][n][tc + e], vf[e], s);
+        acc[n][j] = s;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  {
+    u32x4 kc[KI], vc[VI];
+    int blk = kb0 + w;
+    if (blk < kb1) load(blk, kc, vc);
+    for (; blk < kb1; blk += NW) {
+      u32x4 kn[KI] = {}, vn[VI] = {};
+      const int nb = blk + NW;
+      if (nb < kb1) load(nb, kn, vn);
+      process(blk, kc, vc);
+#pragma unroll
+      for (int i = 0; i < KI; ++i) kc[i] = kn[i];
+#pragma unroll
+      for (int j = 0; j < VI; ++j) vc[j] = vn[j];
+    }
+  }
+
+  // ---- merge the waves --------------------------------------------------------
+#pragma unroll
+  for (int n = 0; n < NQ; ++n) {
+    const float lt = xor_sum_from<LPT>(l[n]);
+#pragma unroll
+    for (int j = 0; j < VI; ++j) {
+      const float v = group_sum<CPR>(acc[n][j]);
+      if (lane % CPR == 0) s_acc[w][n][j * DPI + lane / CPR] = v;
+    }
+    if (lane == 0) { s_m[w][n] = m[n]; s_l[w][n] = lt; }
+  }
+  __syncthreads();
+
+  const bool split = a.write_partials || it.num_parts > 1;
+  for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
+    const int n = idx / D, d = idx % D;
+    float M = s_m[0][n];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, s_m[ww][n]);
+    float lsum = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = fast_exp2((s_m[ww][n] - M) * c);
+        lsum += f * s_l[ww][n];
+        o += f * s_acc[ww][n][d];
+      }
+      o /= lsum;
+    }
+    const int tok = n / hc;
+    const int h = g * G + it.head_begin + n % hc;
+    const size_t row = (size_t)row0 + it.q_begin + tok;
+    if (!split) {
+      store_elem<DT>(a.o, (row * Hq + h) * D + d, o);
+    } else {
+      const size_t pi = (row * Hq + h) * a.part_stride + it.part;
+      a.part_o[pi * D + d] = o;
+      if (d == 0) {
+        a.part_m[pi] = (M == -INFINITY) ? -INFINITY : M * a.scale;
+        a.part_l[pi] = lsum;
+      }
+    }
+  }
+}
+
+template <int DT, int D>
+static hipError_t launch_vec_d(const AttnArgs& args, int rows, hipStream_t stream) {
+  dim3 grid(args.num_items), block(256);
+  switch (rows) {
+    case 1: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 1>), grid, block, 0, stream, args); break;
+    case 2: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 2>), grid, block, 0, stream, args); break;
+    case 4: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 4>), grid, block, 0, stream, args); break;
+    default: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 8>), grid, block, 0, stream, args); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_vec_dt(const AttnArgs& args, int head_dim, int rows, hipStream_t stream) {
+  return head_dim == 64 ? launch_vec_d<DT, 64>(args, rows, stream) : launch_vec_d<DT, 128>(args, rows, stream);
+}
+
+hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int head_dim, int rows_per_item,
+                              hipStream_t stream) {
+  if (args.num_items == 0) return hipSuccess;
+  switch (dtype) {
+    case kF32: return launch_vec_dt<kF32>(args, head_dim, rows_per_item, stream);
+    case kF16: return launch_vec_dt<kF16>(args, head_dim, rows_per_item, stream);
+    default: return launch_vec_dt<kBF16>(args, head_dim, rows_per_item, stream);
+  }
+}
+
+}  // namespace pk

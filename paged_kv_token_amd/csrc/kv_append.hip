@@ -1,0 +1,114 @@
+// KV append: slot-mapped copy of new K/V rows into the paged pools.
+//
+// A token's slot is physical_block * 16 + offset: the block the caller
+// allocated for it ("LLM上下文缓存与状态复用机制的分析和探索", section 3.1:
+// fixed-size blocks allocated on demand in non-contiguous memory).
+//
+// Pools: K [num_blocks][Hkv][16][D] (token rows), V [num_blocks][Hkv][D][16]
+// (dim rows).  One workgroup copies 16 consecutive new tokens of one KV head:
+// K rows go straight to their slots with 16-byte stores; V rows are staged in
+// LDS and written as 16-byte runs of consecutive tokens of one dim row when
+// the slots of a token run are consecutive and aligned (the usual case: a
+// request's new tokens fill its blocks in order), else one element at a time.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pk {
+
+template <int EB, int D>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ k_new,
+                                                        const uint8_t* __restrict__ v_new,
+                                                        uint8_t* __restrict__ k_pool,
+                                                        uint8_t* __restrict__ v_pool,
+                                                        const int32_t* __restrict__ slots, int num_tokens,
+                                                        int num_kv_heads) {
+  constexpr int ROW = D * EB;        // bytes of one token's row for one head
+  constexpr int CPR = ROW / 16;      // 16-byte chunks per row
+  constexpr int EPC = 16 / EB;       // elements per 16-byte chunk
+  constexpr int TG = 16 / EPC;       // 16-byte token runs per V dim row
+  __shared__ int s_slot[16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[16 * ROW];
+
+  const int t0 = blockIdx.x * 16;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < 16) s_slot[tid] = (t0 + tid < num_tokens) ? slots[t0 + tid] : -1;
+  __syncthreads();
+
+  const size_t tile_bytes = (size_t)16 * ROW;
+  for (int c = tid; c < 16 * CPR; c += 256) {
+    const int tok = c / CPR, wc = c % CPR;
+    const int s = s_slot[tok];
+    if (s >= 0) {
+      const size_t src = ((size_t)(t0 + tok) * num_kv_heads + g) * ROW + (size_t)wc * 16;
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + src);
+      const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+      *reinterpret_cast<u32x4*>(k_pool + (blk * num_kv_heads + g) * tile_bytes + off * ROW + (size_t)wc * 16) = kv;
+      *reinterpret_cast<u32x4*>(s_v + tok * ROW + wc * 16) = *reinterpret_cast<const u32x4*>(v_new + src);
+    }
+  }
+  __syncthreads();
+
+  for (int c = tid; c < D * TG; c += 256) {
+    const int tg = c % TG, d = c / TG;
+    const int ts = tg * EPC;
+    const int s0 = s_slot[ts];
+    bool run = (s0 >= 0) && (s0 % EPC) == 0;
+#pragma unroll
+    for (int e = 1; e < EPC; ++e) run = run && (s_slot[ts + e] == s0 + e);
+    if (run) {
+      u32x4 out;
+      if constexpr (EB == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = *reinterpret_cast<const uint32_t*>(s_v + (ts + e) * ROW + d * 4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(s_v + (ts + 2 * e) * ROW + d * 2);
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(s_v + (ts + 2 * e + 1) * ROW + d * 2);
+          out[e] = lo | (hi << 16);
+        }
+      }
+      const size_t blk = (size_t)(s0 >> 4), off = (size_t)(s0 & 15);
+      *reinterpret_cast<u32x4*>(v_pool + (blk * num_kv_heads + g) * tile_bytes + (size_t)d * 16 * EB + off * EB) = out;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int s = s_slot[ts + e];
+        if (s < 0) continue;
+        const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+        uint8_t* dst = v_pool + (blk * num_kv_heads + g) * tile_bytes + (size_t)d * 16 * EB + off * EB;
+        if constexpr (EB == 4) {
+          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(s_v + (ts + e) * ROW + d * 4);
+        } else {
+          *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(s_v + (ts + e) * ROW + d * 2);
+        }
+      }
+    }
+  }
+}
+
+template <int EB, int D>
+static hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                const int32_t* slots, int num_tokens, int num_kv_heads, hipStream_t stream) {
+  dim3 grid((num_tokens + 15) / 16, num_kv_heads);
+  hipLaunchKernelGGL((kv_append_kernel<EB, D>), grid, dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                     static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slots, num_tokens,
+                     num_kv_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                            const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                            int elem_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  if (elem_bytes == 4) {
+    return head_dim == 64 ? launch_append<4, 64>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads, stream)
+                          : launch_append<4, 128>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads, stream);
+  }
+  return head_dim == 64 ? launch_append<2, 64>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads, stream)
+                        : launch_append<2, 128>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads, stream);
+}
+
+}  // namespace pk

@@ -1,0 +1,82 @@
+// Merge of split-KV partials into the attention output.
+//
+// "PersistentKV: Page-Aware Decode Scheduling for Long-Context LLM Serving on
+// Commodity GPUs", section 2: a long context is cut into partitions handled
+// in parallel and their results are merged.  For one (row, head) with
+// partials (m_k, l_k, O_k): M = max m_k over partitions with l_k > 0,
+// w_k = l_k exp(m_k - M), O = sum_k w_k O_k / sum_k w_k.
+//
+// One wave per (row, head): lanes read the P (m, l) pairs, reduce the max and
+// the weight sum across the wave, park the weights in LDS, then stream the P
+// partial rows of D fp32 values with coalesced loads (lane = dim).
+#include "device_common.h"
+#include "launch.h"
+
+namespace pk {
+
+constexpr int kMaxMergePartitions = 256;
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_m,
+                                                          const float* __restrict__ part_l, int rows, int P,
+                                                          uint8_t* __restrict__ o) {
+  __shared__ float s_w[4][kMaxMergePartitions];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int rh = blockIdx.x * 4 + wv;
+  if (rh >= rows) return;  // whole wave leaves together; no block barrier follows
+  const size_t base = (size_t)rh * P;
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  float M = -INFINITY;
+  for (int p = lane; p < P; p += 64) {
+    if (part_l[base + p] > 0.f) M = fmaxf(M, part_m[base + p]);
+  }
+  M = xor_max_from<1>(M);
+  float W = 0.f;
+  for (int p = lane; p < P; p += 64) {
+    const float l = part_l[base + p];
+    const float wgt = (l > 0.f) ? l * fast_exp2((part_m[base + p] - M) * kLog2e) : 0.f;
+    s_w[wv][p] = wgt;
+    W += wgt;
+  }
+  W = xor_sum_from<1>(W);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float inv = (W > 0.f) ? 1.f / W : 0.f;
+#pragma unroll
+  for (int d0 = 0; d0 < D; d0 += 64) {
+    const int d = d0 + lane;
+    float acc = 0.f;
+    for (int p = 0; p < P; ++p) {
+      const float wgt = s_w[wv][p];
+      if (wgt != 0.f) acc = fmaf(wgt, part_o[(base + p) * D + d], acc);
+    }
+    store_elem<DT>(o, (size_t)rh * D + d, acc * inv);
+  }
+}
+
+template <int DT>
+static hipError_t launch_merge_dt(const float* po, const float* pm, const float* pl, int rows, int head_dim, int P,
+                                  void* o, hipStream_t stream) {
+  dim3 grid((rows + 3) / 4), block(256);
+  if (head_dim == 64)
+    hipLaunchKernelGGL((split_merge_kernel<DT, 64>), grid, block, 0, stream, po, pm, pl, rows, P, (uint8_t*)o);
+  else
+    hipLaunchKernelGGL((split_merge_kernel<DT, 128>), grid, block, 0, stream, po, pm, pl, rows, P, (uint8_t*)o);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows,
+                              int head_dim, int num_partitions, int dtype, void* o, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  switch (dtype) {
+    case kF32: return launch_merge_dt<kF32>(part_o, part_m, part_l, rows, head_dim, num_partitions, o, stream);
+    case kF16: return launch_merge_dt<kF16>(part_o, part_m, part_l, rows, head_dim, num_partitions, o, stream);
+    default: return launch_merge_dt<kBF16>(part_o, part_m, part_l, rows, head_dim, num_partitions, o, stream);
+  }
+}
+
+}  // namespace pk

@@ -19,11 +19,13 @@ Conventions (fixed here, used by both the oracle and the GPU path):
   append, its KV covers positions ``[0, L_r)`` with ``L_r = H_r + n_r``.  Its
   query rows are positions ``[0, E_r)`` followed by ``[H_r, H_r + n_r)``, so
   ``q_r = E_r + n_r``.  Rows are packed request by request (``cu_q_lens``).
-* Values: per request and per tensor an independent NumPy ``default_rng``
-  stream keyed ``(seed, tensor tag, request)`` draws float32 standard normals,
-  multiplied by 0.5 and rounded to nearest-even into the storage dtype.  K and
-  V are drawn for all ``L_r`` positions in position order, so any single
-  request can be regenerated without the rest of the batch.
+* Values: rows of each tensor (Q rows, K/V positions) are drawn in chunks
+  of 1024 rows; chunk c of tensor tag of request r comes from its own NumPy
+  ``default_rng`` stream keyed ``(seed, tag, r, c)``: float32 standard
+  normals, multiplied by 0.5, rounded to nearest-even into the storage dtype.
+  K and V are drawn for all ``L_r`` positions in position order, so any
+  single request (or chunk) can be regenerated alone, and chunks can be
+  drawn in parallel threads.
 * Storage dtypes: ``f32`` -> ``np.float32``, ``f16`` -> ``np.float16``,
   ``bf16`` -> ``np.uint16`` holding the bfloat16 bit pattern.
 """
@@ -31,6 +33,8 @@ Conventions (fixed here, used by both the oracle and the GPU path):
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Callable, Iterator, Optional
 
@@ -47,6 +51,16 @@ CONFIG_NAMES = (
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 BASE_SEED = 20231209
 _TAG_Q, _TAG_K, _TAG_V = 1, 2, 3
+ROW_CHUNK = 1024
+_WORKERS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+_pool: Optional[ThreadPoolExecutor] = None
+
+
+def _thread_pool() -> ThreadPoolExecutor:
+    global _pool
+    if _pool is None:
+        _pool = ThreadPoolExecutor(max_workers=_WORKERS, thread_name_prefix="workloads")
+    return _pool
 
 
 def storage_dtype(dtype: str):
@@ -166,37 +180,57 @@ class Batch:
         return -(-int(self.context_lens[r]) // self.block_size)
 
     # ---- values -----------------------------------------------------------
-    def _rng(self, tag: int, r: int) -> np.random.Generator:
-        return np.random.default_rng([self.seed, tag, r])
+    def _draw_chunk(self, tag: int, r: int, c: int, rows: int, width) -> np.ndarray:
+        rng = np.random.default_rng([self.seed, tag, r, c])
+        x = rng.standard_normal((rows, *width), dtype=np.float32)
+        x *= np.float32(self.value_scale)
+        return _to_storage(x, self.dtype)
 
-    def _draw(self, tag: int, r: int, shape) -> np.ndarray:
-        return self._rng(tag, r).standard_normal(shape, dtype=np.float32) * np.float32(self.value_scale)
+    def _draw_rows(self, tag: int, r: int, nrows: int, width, parallel: bool) -> np.ndarray:
+        out = np.empty((nrows, *width), dtype=storage_dtype(self.dtype))
+        nch = -(-nrows // ROW_CHUNK)
 
-    def request_q(self, r: int) -> np.ndarray:
+        def work(c):
+            lo, hi = c * ROW_CHUNK, min(nrows, (c + 1) * ROW_CHUNK)
+            out[lo:hi] = self._draw_chunk(tag, r, c, hi - lo, width)
+
+        if parallel and nch > 1:
+            list(_thread_pool().map(work, range(nch)))
+        else:
+            for c in range(nch):
+                work(c)
+        return out
+
+    def request_q(self, r: int, parallel: bool = True) -> np.ndarray:
         shape = (int(self.q_lens[r]), self.num_heads, self.head_dim)
-        x = self.q_fn(r) if self.q_fn is not None else self._draw(_TAG_Q, r, shape)
-        return _to_storage(np.asarray(x, dtype=np.float32).reshape(shape), self.dtype)
+        if self.q_fn is not None:
+            return _to_storage(np.asarray(self.q_fn(r), dtype=np.float32).reshape(shape), self.dtype)
+        return self._draw_rows(_TAG_Q, r, shape[0], shape[1:], parallel)
 
-    def request_kv(self, r: int):
+    def request_kv(self, r: int, parallel: bool = True):
         """K and V of every position of request r, [L_r][Hkv][d] each, position order."""
         shape = (int(self.context_lens[r]), self.num_kv_heads, self.head_dim)
-        k = self.k_fn(r) if self.k_fn is not None else self._draw(_TAG_K, r, shape)
-        v = self.v_fn(r) if self.v_fn is not None else self._draw(_TAG_V, r, shape)
-        k = _to_storage(np.asarray(k, dtype=np.float32).reshape(shape), self.dtype)
-        v = _to_storage(np.asarray(v, dtype=np.float32).reshape(shape), self.dtype)
+        if self.k_fn is not None:
+            k = _to_storage(np.asarray(self.k_fn(r), dtype=np.float32).reshape(shape), self.dtype)
+        else:
+            k = self._draw_rows(_TAG_K, r, shape[0], shape[1:], parallel)
+        if self.v_fn is not None:
+            v = _to_storage(np.asarray(self.v_fn(r), dtype=np.float32).reshape(shape), self.dtype)
+        else:
+            v = self._draw_rows(_TAG_V, r, shape[0], shape[1:], parallel)
         return k, v
 
     def q_all(self) -> np.ndarray:
         sd = storage_dtype(self.dtype)
         if self.total_q == 0:
             return np.zeros((0, self.num_heads, self.head_dim), dtype=sd)
-        return np.concatenate([self.request_q(r) for r in range(self.num_reqs)], axis=0)
+        parts = list(_thread_pool().map(lambda r: self.request_q(r, parallel=False), range(self.num_reqs)))
+        return np.concatenate(parts, axis=0)
 
     def new_kv(self):
         """K/V of the query rows' own positions, [T][Hkv][d], row order."""
         ks, vs = [], []
-        for r in range(self.num_reqs):
-            k, v = self.request_kv(r)
+        for r, k, v, _, _ in self.iter_requests():
             pos = self.query_positions(r)
             ks.append(k[pos])
             vs.append(v[pos])
@@ -204,12 +238,27 @@ class Batch:
         empty = np.zeros((0, self.num_kv_heads, self.head_dim), dtype=sd)
         return (np.concatenate(ks, axis=0) if ks else empty, np.concatenate(vs, axis=0) if vs else empty)
 
-    def iter_requests(self) -> Iterator[tuple]:
-        """Per request: (r, K all positions, V all positions, cached slots, cached positions)."""
-        for r in range(self.num_reqs):
-            k, v = self.request_kv(r)
+    def iter_requests(self, window: Optional[int] = None) -> Iterator[tuple]:
+        """Per request: (r, K all positions, V all positions, cached slots, cached positions).
+
+        Requests are drawn ahead in worker threads (at most ``window`` at a
+        time) and yielded in order.
+        """
+        window = window or 2 * _WORKERS
+
+        def one(r):
+            k, v = self.request_kv(r, parallel=False)
             pos = self.cached_positions(r)
-            yield r, k, v, self.slots_for(r, pos), pos
+            return r, k, v, self.slots_for(r, pos), pos
+
+        pending = []
+        nxt = 0
+        pool = _thread_pool()
+        while nxt < self.num_reqs or pending:
+            while nxt < self.num_reqs and len(pending) < window:
+                pending.append(pool.submit(one, nxt))
+                nxt += 1
+            yield pending.pop(0).result()
 
 
 def _place_blocks(rng, need: np.ndarray, num_blocks: int, stride: int) -> np.ndarray:
