@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the generalized paged-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one unified batch: plan the work
+list (host) and upload it, append the step's new K/V rows into the paged
+pools (kv_append), and run the attention of every query row over its
+request's paged KV (attn_fwd).  The workload is the Llama-2-13B-shaped mixed
+batch (40 heads, head_dim 128, fp16; 32 conversations with 16-128 new tokens
+plus 32 decode requests, histories of 256-2048 tokens), generated from a
+fixed seed and resident in HBM before the timed region starts.
+
+Prints ONE JSON line with the headline metric (query tokens/s), a roofline
+object for the dominant kernel (per-launch durations come from HIP events the
+library records on its launch stream during the timed region), and the CPU
+oracle timed on this host on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_token_amd as pk  # noqa: E402
+from workloads import config_batch  # noqa: E402
+
+METRIC = "attn query-tokens/s + % HBM BW (decode) / % MFMA peak (prefill), 13B shape"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}   # dense MFMA (fp32: vector peak)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = {
+    "attn_mfma": ["attn_mfma.hip", "device_common.h"],
+    "attn_vector": ["attn_vector.hip", "device_common.h"],
+    "kv_append": ["kv_append.hip", "device_common.h"],
+    "split_merge": ["split_merge.hip", "device_common.h"],
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "paged_kv_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# device-side batch
+# ---------------------------------------------------------------------------
+class DeviceBatch:
+    """A seeded batch resident in HBM: pools filled with its cached history."""
+
+    def __init__(self, batch):
+        import torch
+        self.b = b = batch
+        td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[b.dtype]
+        self.td = td
+        self.k_pool = torch.empty((b.num_blocks, b.num_kv_heads, 16, b.head_dim), dtype=td, device="cuda")
+        self.v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.head_dim, 16), dtype=td, device="cuda")
+        self.k_pool.fill_(float("nan"))
+        self.v_pool.fill_(float("nan"))
+        for r, k, v, slots, pos in b.iter_requests():
+            if len(pos):
+                pk.pensieve_kv_append(self._dev(k[pos]), self._dev(v[pos]), self.k_pool, self.v_pool,
+                                      torch.from_numpy(slots.copy()).cuda())
+        kn, vn = b.new_kv()
+        self.k_new, self.v_new = self._dev(kn), self._dev(vn)
+        self.new_slots = torch.from_numpy(b.new_slots.copy()).cuda()
+        self.q = self._dev(b.q_all())
+        self.o = torch.empty_like(self.q)
+        self.bt = torch.from_numpy(b.block_tables.copy()).cuda()
+        self.ctx = torch.from_numpy(b.context_lens.copy()).cuda()
+        self.cu = torch.from_numpy(b.cu_q_lens.copy()).cuda()
+        self.q_pos = None if b.has_default_positions else torch.from_numpy(b.q_pos.copy()).cuda()
+        self.desc = pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                                 num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
+                                 dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
+                                 context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens)
+        self.ws = torch.empty(max(pk.pensieve_attn_workspace_size(self.desc), 256), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def _dev(self, arr):
+        import torch
+        if self.b.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+    def step(self):
+        pk.pensieve_kv_append(self.k_new, self.v_new, self.k_pool, self.v_pool, self.new_slots)
+        pk.pensieve_attn_fwd(self.desc, self.q, self.k_pool, self.v_pool, self.bt, self.ctx, self.cu, self.q_pos,
+                             self.o, self.ws)
+
+    def split_step(self, P, bufs):
+        po, pm, pl, ws = bufs
+        pk.pensieve_attn_split_partial(self.desc, P, self.q, self.k_pool, self.v_pool, self.bt, self.ctx, self.cu,
+                                       self.q_pos, po, pm, pl, ws)
+        pk.pensieve_attn_split_merge(po, pm, pl, self.o)
+
+    def split_buffers(self, P):
+        import torch
+        b = self.b
+        T = b.total_q
+        return (torch.empty((T, b.num_heads, P, b.head_dim), dtype=torch.float32, device="cuda"),
+                torch.empty((T, b.num_heads, P), dtype=torch.float32, device="cuda"),
+                torch.empty((T, b.num_heads, P), dtype=torch.float32, device="cuda"),
+                torch.empty(max(pk.pensieve_attn_workspace_size(self.desc, P), 256), dtype=torch.uint8,
+                            device="cuda"))
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+def request_bytes(b, r: int) -> int:
+    """Bytes the method must move for request r: its K and V once per KV head,
+    its Q rows in and O rows out, its block-table entries, lengths and positions."""
+    e = b.elem_bytes
+    L, q = int(b.context_lens[r]), int(b.q_lens[r])
+    nblk = -(-L // 16)
+    kv = 2 * L * b.num_kv_heads * b.head_dim * e
+    qo = 2 * q * b.num_heads * b.head_dim * e
+    meta = 4 * nblk + 8 + (0 if b.has_default_positions else 4 * q)
+    return kv + qo + meta
+
+
+def request_flops(b, r: int) -> int:
+    """QK^T and PV over visible (row, key) pairs only: 4 d Hq (p + 1) per row."""
+    pos = b.query_positions(r)
+    return int(4 * b.head_dim * b.num_heads * int((pos + 1).sum()))
+
+
+def kernel_requests(dev: DeviceBatch, num_partitions: int = 0):
+    """Requests served by each attention kernel (from the library's own plan)."""
+    plan = pk.pensieve_debug_plan(dev.desc, num_partitions)
+    out = {"attn_vector": set(), "attn_mfma": set()}
+    for row in plan:
+        out["attn_mfma" if row[0] == 1 else "attn_vector"].add(int(row[1]))
+    return out
+
+
+def append_bytes(b) -> int:
+    """Read K/V new rows and write them into the pools (+ slot ids)."""
+    return 2 * 2 * b.total_q * b.num_kv_heads * b.head_dim * b.elem_bytes + 4 * b.total_q
+
+
+# ---------------------------------------------------------------------------
+def time_steps(fn, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` calls with library tracing on; returns (ms/step, trace)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    pk.pensieve_trace_read()
+    pk.pensieve_trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pk.pensieve_trace_enable(False)
+    trace = pk.pensieve_trace_read()
+    return (t1 - t0) * 1e3 / steps, trace
+
+
+def summarize_trace(trace, steps: int):
+    per = {}
+    for name, items, ms in trace:
+        d = per.setdefault(name, {"launches": 0, "total_ms": 0.0, "items": items})
+        d["launches"] += 1
+        d["total_ms"] += ms
+    for d in per.values():
+        d["avg_ms"] = d["total_ms"] / d["launches"]
+        d["per_step_ms"] = d["total_ms"] / steps
+    return per
+
+
+def roofline_for(b, dev, per, kernel: str, counters):
+    reqs = kernel_requests(dev)
+    if kernel in ("attn_vector", "attn_mfma"):
+        rs = sorted(reqs[kernel])
+        nbytes = sum(request_bytes(b, r) for r in rs)
+        flops = sum(request_flops(b, r) for r in rs)
+    elif kernel == "kv_append":
+        nbytes, flops = append_bytes(b), 0
+    else:
+        nbytes, flops = 0, 0
+    avg_s = per[kernel]["avg_ms"] * 1e-3
+    intensity = flops / nbytes if nbytes else 0.0
+    ridge = MFMA_PEAK_TFLOPS[b.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = None
+    if counters:
+        c = counters.get(f"{kernel}@{b.name}")
+        if c and c.get("source_sha") == source_digest(kernel):
+            traffic = c.get("traffic_bytes_per_launch")
+    if intensity < ridge:
+        achieved = nbytes / avg_s / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "avg_launch_ms": round(per[kernel]["avg_ms"], 4)}
+    achieved = flops / avg_s / 1e12
+    peak = MFMA_PEAK_TFLOPS[b.dtype]
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic, "algorithmic_bytes": nbytes,
+            "algorithmic_flops": flops, "avg_launch_ms": round(per[kernel]["avg_ms"], 4)}
+
+
+def load_counters():
+    if not os.path.exists(COUNTERS_FILE):
+        return {}
+    with open(COUNTERS_FILE) as fh:
+        return json.load(fh)
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(b, budget_s: float):
+    """The CPU oracle (as it stands) on this host: all requests, as many query heads as fit the budget."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from oracle_helpers import oracle_pools
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    pools = oracle_pools(b)
+    q = b.q_all()
+    qpos = None if b.has_default_positions else b.q_pos
+    done, elapsed = 0, 0.0
+    chunk = 2
+    while done < b.num_heads and elapsed < budget_s:
+        heads = list(range(done, min(done + chunk, b.num_heads)))
+        t0 = time.perf_counter()
+        oracle.paged_attention(q, pools[0], pools[1], b.block_tables, b.context_lens, b.cu_q_lens, qpos,
+                               b.softmax_scale, b.dtype, heads=heads)
+        elapsed += time.perf_counter() - t0
+        done += len(heads)
+    rate = b.total_q * (done / b.num_heads) / elapsed
+    return {"value": round(rate, 2), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"all {b.num_reqs} requests x query heads 0..{done - 1} of {b.num_heads} "
+                      f"({elapsed:.1f} s, float64 NumPy; rate scaled to all heads)"}
+
+
+def secondary(index: int, steps: int, warmup: int, counters):
+    """Other workloads of the same path, measured the same way (reported beside the headline)."""
+    import torch
+    b = config_batch(index)
+    dev = DeviceBatch(b)
+    out = {"workload": b.name, "total_q": b.total_q}
+    ms, trace = time_steps(lambda: pk.pensieve_attn_fwd(dev.desc, dev.q, dev.k_pool, dev.v_pool, dev.bt, dev.ctx,
+                                                        dev.cu, dev.q_pos, dev.o, dev.ws), steps, warmup)
+    per = summarize_trace(trace, steps)
+    attn = {k: v for k, v in per.items() if k.startswith("attn")}
+    dom = max(attn, key=lambda k: attn[k]["total_ms"])
+    out["attn_ms"] = round(ms, 4)
+    out["query_tokens_per_s"] = round(b.total_q / (ms * 1e-3), 1)
+    out["kernels_ms"] = {k: round(v["avg_ms"], 4) for k, v in per.items()}
+    out["roofline"] = roofline_for(b, dev, per, dom, counters)
+    if index == 4:
+        bufs = dev.split_buffers(32)
+        ms2, trace2 = time_steps(lambda: dev.split_step(32, bufs), steps, warmup)
+        per2 = summarize_trace(trace2, steps)
+        out["split32_ms"] = round(ms2, 4)
+        out["split32_kernels_ms"] = {k: round(v["avg_ms"], 4) for k, v in per2.items()}
+        total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
+        out["split32_hbm_frac"] = round(total_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        del bufs
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path needs no collective); --gpus {args.gpus} is not run.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pk.load_library()
+    counters = load_counters()
+
+    b = config_batch(1)
+    log(f"workload {b.name}: R={b.num_reqs} T={b.total_q} context tokens={int(b.context_lens.sum())}")
+    dev = DeviceBatch(b)
+    ms, trace = time_steps(dev.step, args.steps, args.warmup)
+    per = summarize_trace(trace, args.steps)
+    dom = max(per, key=lambda k: per[k]["total_ms"])
+    log(f"{ms:.4f} ms/step; kernels: " + ", ".join(f"{k} {v['avg_ms']:.4f} ms x{v['launches'] // args.steps}"
+                                                     for k, v in per.items()))
+    roof = roofline_for(b, dev, per, dom, counters)
+    result = {
+        "metric": METRIC, "value": round(b.total_q / (ms * 1e-3), 1), "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
+        "config": {"workload": b.name, "requests": b.num_reqs, "decode_requests": int((b.new_lens == 1).sum()),
+                   "total_q": b.total_q, "context_tokens": int(b.context_lens.sum()), "num_heads": b.num_heads,
+                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": 16, "seed": b.seed},
+        "roofline": roof,
+        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per.items()},
+    }
+    # The attention as a whole (both kernels) against the HBM roofline.
+    attn_ms = sum(v["per_step_ms"] for k, v in per.items() if k.startswith("attn"))
+    total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
+    result["attn_total"] = {"ms": round(attn_ms, 4), "bytes": total_bytes,
+                            "hbm_frac": round(total_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dev
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        result["secondary"] = []
+        for idx in (2, 3, 4):
+            log(f"secondary workload {idx}")
+            result["secondary"].append(secondary(idx, max(20, args.steps // 4), 5, counters))
+    if not args.no_cpu:
+        log("cpu_baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

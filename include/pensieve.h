@@ -185,6 +185,26 @@ pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part
 pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num_partitions,
                                     int32_t* items_host, int32_t max_items, int32_t* num_items);
 
+/*
+ * Per-launch timing trace.  While enabled, every kernel the library
+ * launches is bracketed by a pair of hipEvents recorded on the launch
+ * stream.  pensieve_trace_read waits for the recorded launches to finish,
+ * writes up to max_records records {kernel, work items, milliseconds}
+ * (kernel: 0 kv_append, 1 vector attention, 2 matrix-core attention,
+ * 3 split merge), sets *num_records to the number written, and clears the
+ * trace.  The events come from a pool created on first enable (per device)
+ * and reused.  Tracing is off by default and costs nothing when off.
+ */
+typedef struct pensieve_trace_record {
+  int32_t kernel;
+  int32_t items;
+  float ms;
+} pensieve_trace_record;
+
+pensieve_status pensieve_trace_enable(int32_t enable);
+pensieve_status pensieve_trace_read(pensieve_trace_record* records_host, int32_t max_records,
+                                    int32_t* num_records);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,5 +21,7 @@ from .binding import (  # noqa: F401
     pensieve_attn_workspace_size,
     pensieve_debug_plan,
     pensieve_kv_append,
+    pensieve_trace_enable,
+    pensieve_trace_read,
     pensieve_version,
 )

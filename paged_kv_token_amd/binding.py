@@ -29,7 +29,9 @@ PENSIEVE_FLAG_VECTOR_ONLY = 1
 EXPORTED = (
     "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",
     "pensieve_attn_fwd", "pensieve_attn_split_partial", "pensieve_attn_split_merge", "pensieve_debug_plan",
+    "pensieve_trace_enable", "pensieve_trace_read",
 )
+TRACE_KERNELS = {0: "kv_append", 1: "attn_vector", 2: "attn_mfma", 3: "split_merge"}
 
 
 class PensieveError(RuntimeError):
@@ -57,6 +59,10 @@ class BatchDesc(ctypes.Structure):
     ]
 
 
+class TraceRecord(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("items", ctypes.c_int32), ("ms", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -80,6 +86,8 @@ def load_library(path: Optional[str] = None):
                                                 ctypes.c_size_t, vp]
     lib.pensieve_attn_split_merge.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.pensieve_debug_plan.argtypes = [dp, i32, i32p, i32, i32p]
+    lib.pensieve_trace_enable.argtypes = [i32]
+    lib.pensieve_trace_read.argtypes = [ctypes.POINTER(TraceRecord), i32, i32p]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -200,3 +208,16 @@ def pensieve_debug_plan(desc: BatchDesc, num_partitions: int = 0) -> np.ndarray:
     _check(lib.pensieve_debug_plan(ctypes.byref(desc), num_partitions,
                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n)))
     return out[:n.value]
+
+
+def pensieve_trace_enable(enable: bool = True) -> None:
+    _check(load_library().pensieve_trace_enable(1 if enable else 0))
+
+
+def pensieve_trace_read(max_records: int = 1 << 16):
+    """Per-launch records [(kernel name, work items, ms)] since the last read."""
+    buf = (TraceRecord * max_records)()
+    n = ctypes.c_int32(0)
+    _check(load_library().pensieve_trace_read(buf, max_records, ctypes.byref(n)))
+    return [(TRACE_KERNELS.get(buf[i].kernel, str(buf[i].kernel)), int(buf[i].items), float(buf[i].ms))
+            for i in range(n.value)]

@@ -250,6 +250,51 @@ hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t
   return hipSuccess;
 }
 
+// ---- per-launch timing trace ------------------------------------------------------------
+enum TraceKernel { kTraceAppend = 0, kTraceVector = 1, kTraceMatrix = 2, kTraceMerge = 3 };
+
+struct TraceEntry {
+  int kernel;
+  int items;
+  hipEvent_t start, stop;
+};
+
+std::mutex g_trace_mu;
+bool g_trace_on = false;
+std::vector<TraceEntry> g_trace;
+std::vector<hipEvent_t> g_event_pool;
+constexpr size_t kMaxTraceEntries = 1 << 16;
+
+hipEvent_t trace_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events when tracing is on.
+struct TraceScope {
+  bool active = false;
+  TraceEntry entry{};
+  hipStream_t stream;
+  TraceScope(int kernel, int items, hipStream_t s) : stream(s) {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    if (!g_trace_on || g_trace.size() >= kMaxTraceEntries) return;
+    entry = {kernel, items, trace_event(), trace_event()};
+    if (!entry.start || !entry.stop) return;
+    active = hipEventRecord(entry.start, stream) == hipSuccess;
+  }
+  ~TraceScope() {
+    if (!active) return;
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    if (hipEventRecord(entry.stop, stream) == hipSuccess) g_trace.push_back(entry);
+  }
+};
+
 pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::AttnArgs& args, void* workspace,
                          hipStream_t stream) {
   hipError_t e = stage_to_device(workspace, plan.items.data(), plan.items.size() * sizeof(pk::WorkItem), stream);
@@ -259,6 +304,7 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     pk::AttnArgs a = args;
     a.items = dev_items + s.begin;
     a.num_items = s.count;
+    TraceScope trace(s.kernel == kMatrix ? kTraceMatrix : kTraceVector, s.count, stream);
     if (s.kernel == kMatrix)
       e = pk::launch_attn_mfma(a, d->dtype, d->head_dim, s.param, stream);
     else
@@ -318,6 +364,7 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
     return fail(PENSIEVE_ERR_INVALID_ARG, "a device pointer is NULL");
+  TraceScope trace(kTraceAppend, num_tokens, static_cast<hipStream_t>(stream));
   hipError_t e = pk::launch_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
                                       elem_bytes(dtype), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
@@ -396,6 +443,7 @@ pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part
   if (rows == 0) return ok();
   if (rows > (1LL << 31) - 4) return fail(PENSIEVE_ERR_UNSUPPORTED, "too many rows");
   if (!part_o || !part_m || !part_l || !o) return fail(PENSIEVE_ERR_INVALID_ARG, "a pointer is NULL");
+  TraceScope trace(kTraceMerge, (int)rows, static_cast<hipStream_t>(stream));
   hipError_t e = pk::launch_split_merge(part_o, part_m, part_l, (int)rows, head_dim, num_partitions, dtype, o,
                                         static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "split merge launch");
@@ -424,6 +472,40 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
     o[6] = p.w.num_parts;
     o[7] = (int32_t)std::min<long long>(p.cost, 0x7fffffff);
   }
+  return ok();
+}
+
+pensieve_status pensieve_trace_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  g_trace_on = enable != 0;
+  return ok();
+}
+
+pensieve_status pensieve_trace_read(pensieve_trace_record* records_host, int32_t max_records, int32_t* num_records) {
+  if (!num_records || (max_records > 0 && !records_host)) return fail(PENSIEVE_ERR_INVALID_ARG, "NULL output");
+  std::vector<TraceEntry> entries;
+  {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    entries.swap(g_trace);
+  }
+  int32_t n = 0;
+  hipError_t err = hipSuccess;
+  for (const TraceEntry& t : entries) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    if (n < max_records) records_host[n++] = {t.kernel, t.items, ms};
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    for (const TraceEntry& t : entries) {
+      g_event_pool.push_back(t.start);
+      g_event_pool.push_back(t.stop);
+    }
+  }
+  *num_records = n;
+  if (err != hipSuccess) return hip_fail(err, "trace read");
   return ok();
 }
 
