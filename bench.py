@@ -289,6 +289,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device (a reference kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path needs no collective); --gpus {args.gpus} is not run.",
@@ -300,6 +302,16 @@ def main():
         sys.exit(1)
     pk.load_library()
     counters = load_counters()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.copy_calibration} MiB x 2")
+        del src, dst
 
     b = config_batch(1)
     log(f"workload {b.name}: R={b.num_reqs} T={b.total_q} context tokens={int(b.context_lens.sum())}")
