@@ -176,11 +176,11 @@ pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part
 /*
  * Host-only introspection of the work list pensieve_attn_fwd
  * (num_partitions == 0) or pensieve_attn_split_partial would build for this
- * batch.  Writes up to max_items records of 8 int32 each:
+ * batch.  Writes up to max_items records of 10 int32 each:
  *   {kernel, request, kv_head, first row in request, rows, partition,
- *    partitions, estimated cost}
- * with kernel 0 = vector path, 1 = matrix-core path, and sets *num_items to
- * the full count.  No GPU is touched.
+ *    partitions, estimated cost, first query head of the group, heads}
+ * with kernel 0 = vector path, 1 = matrix-core path, in launch order, and
+ * sets *num_items to the full count.  No GPU is touched.
  */
 pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num_partitions,
                                     int32_t* items_host, int32_t max_items, int32_t* num_items);

@@ -200,11 +200,11 @@ def pensieve_attn_split_merge(part_o, part_m, part_l, o, stream=None):
 
 
 def pensieve_debug_plan(desc: BatchDesc, num_partitions: int = 0) -> np.ndarray:
-    """Work list the library would launch: int32 [n][8] (see pensieve.h)."""
+    """Work list the library would launch: int32 [n][10] (see pensieve.h)."""
     lib = load_library()
     n = ctypes.c_int32(0)
     _check(lib.pensieve_debug_plan(ctypes.byref(desc), num_partitions, None, 0, ctypes.byref(n)))
-    out = np.zeros((max(n.value, 1), 8), dtype=np.int32)
+    out = np.zeros((max(n.value, 1), 10), dtype=np.int32)
     _check(lib.pensieve_debug_plan(ctypes.byref(desc), num_partitions,
                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n)))
     return out[:n.value]

@@ -462,7 +462,7 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
   *num_items = (int32_t)plan.planned.size();
   for (int i = 0; i < (int)plan.planned.size() && i < max_items; ++i) {
     const PlannedItem& p = plan.planned[i];
-    int32_t* o = items_host + 8 * i;
+    int32_t* o = items_host + 10 * i;
     o[0] = p.kernel;
     o[1] = p.w.req;
     o[2] = p.w.kv_head;
@@ -471,6 +471,8 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
     o[5] = p.w.part;
     o[6] = p.w.num_parts;
     o[7] = (int32_t)std::min<long long>(p.cost, 0x7fffffff);
+    o[8] = p.w.head_begin;
+    o[9] = p.w.head_count;
   }
   return ok();
 }

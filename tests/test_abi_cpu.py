@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point,
+rejects bad arguments on the host, and plans every (row, head) exactly once."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_token_amd as pk
+from paged_kv_token_amd import binding
+from workloads import config_batch, custom_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from paged_kv_token_amd.build import build
+        build(verbose=False)
+    return pk.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pensieve.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pensieve_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_version_string(lib):
+    assert "gfx950" in pk.pensieve_version()
+
+
+def desc_for(b, **over):
+    kw = dict(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, num_blocks=b.num_blocks,
+              block_table_stride=b.block_table_stride, dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype],
+              softmax_scale=b.softmax_scale, context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens)
+    kw.update(over)
+    return pk.make_desc(**kw)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(num_kv_heads=3), 1), (dict(head_dim=96), 2), (dict(block_size=32), 2), (dict(dtype=7), 2),
+    (dict(num_blocks=0), 1), (dict(block_table_stride=1), 1), (dict(softmax_scale=0.0), 1),
+    (dict(softmax_scale=-1.0), 1), (dict(flags=8), 1),
+    (dict(context_lens_host=[4, 5, 6], cu_q_lens_host=[0, 5, 6, 7]), 1),   # q > L
+    (dict(context_lens_host=[4, 5, 6], cu_q_lens_host=[1, 2, 3, 4]), 1),   # cu[0] != 0
+    (dict(context_lens_host=[4, 5, 6], cu_q_lens_host=[0, 2, 1, 2]), 1),   # decreasing
+    (dict(context_lens_host=[4, -1, 6], cu_q_lens_host=[0, 1, 1, 2]), 1),
+])
+def test_bad_descriptors_are_rejected(lib, over, status):
+    b = custom_batch([10, 20, 30], [1, 2, 3], num_heads=4, num_kv_heads=2, head_dim=64, dtype="f16", seed=1)
+    with pytest.raises(pk.PensieveError) as ei:
+        pk.pensieve_attn_workspace_size(desc_for(b, **over))
+    assert ei.value.status == status
+    assert lib.pensieve_last_error().decode()
+
+
+def test_null_pointers_rejected_without_gpu(lib):
+    b = custom_batch([10], [2], num_heads=4, num_kv_heads=4, head_dim=64, dtype="f16", seed=1)
+    d = desc_for(b)
+    st = lib.pensieve_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None, None, None, 0, None)
+    assert st == 1
+    st = lib.pensieve_kv_append(None, None, None, None, None, 5, 4, 64, 16, 10, 1, None)
+    assert st == 1
+    st = lib.pensieve_kv_append(None, None, None, None, None, 0, 4, 64, 16, 10, 1, None)   # nothing to do
+    assert st == 0
+    st = lib.pensieve_attn_split_merge(None, None, None, 4, 2, 64, 300, 1, None, None)     # P too large
+    assert st == 1
+    assert lib.pensieve_attn_workspace_size(None, 0, None) == 1
+
+
+def _coverage(b, plan, P=1):
+    """Every (row, query head, partition) appears exactly once."""
+    seen = np.zeros((b.total_q, b.num_heads, P), dtype=np.int32)
+    G = b.num_heads // b.num_kv_heads
+    for kern, r, g, q0, qc, part, nparts, cost, h0, hc in plan:
+        assert nparts == P and 0 <= part < P
+        lo = int(b.cu_q_lens[r]) + q0
+        assert q0 + qc <= int(b.q_lens[r])
+        for h in range(g * G + h0, g * G + h0 + hc):
+            seen[lo:lo + qc, h, part] += 1
+    return seen
+
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
+def test_plan_covers_each_row_head_once(lib, index):
+    b = config_batch(index)
+    plan = pk.pensieve_debug_plan(desc_for(b))
+    assert np.all(_coverage(b, plan) == 1)
+    # longest first inside each kernel segment
+    for k in (0, 1):
+        costs = [row[7] for row in plan if row[0] == k]
+        assert costs == sorted(costs, reverse=True) or k == 0   # vector items are grouped by width first
+
+
+@pytest.mark.parametrize("P", [1, 7, 32])
+def test_split_plan_covers_each_partition(lib, P):
+    b = config_batch(4, num_heads=4, max_hist=3000)
+    plan = pk.pensieve_debug_plan(desc_for(b), P)
+    assert np.all(_coverage(b, plan, P) == 1)
+
+
+def test_routing_rules(lib):
+    b = config_batch(1, num_reqs=4, num_heads=8)
+    plan = pk.pensieve_debug_plan(desc_for(b))
+    for kern, r, g, q0, qc, *_ in plan:
+        q = int(b.q_lens[r])
+        assert kern == (1 if q > 8 else 0)
+    plan_v = pk.pensieve_debug_plan(desc_for(b, flags=pk.PENSIEVE_FLAG_VECTOR_ONLY))
+    assert np.all(plan_v[:, 0] == 0) and np.all(plan_v[:, 4] * plan_v[:, 9] <= 8)
+    f32 = custom_batch([100], [50], num_heads=4, num_kv_heads=4, head_dim=64, dtype="f32", seed=2)
+    assert np.all(pk.pensieve_debug_plan(desc_for(f32))[:, 0] == 0)
+
+
+def test_workspace_size_matches_plan(lib):
+    b = config_batch(3)
+    d = desc_for(b)
+    n = len(pk.pensieve_debug_plan(d))
+    ws = pk.pensieve_attn_workspace_size(d)
+    assert ws >= 32 * n and ws % 256 == 0 and ws < 32 * n + 256
