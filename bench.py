@@ -286,6 +286,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, help="index of the seeded workload to time (default: the "
+                    "Llama-2-13B mixed batch); other indices are for profiling runs")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
@@ -313,7 +315,7 @@ def main():
         log(f"calibration copy: {args.copy_calibration} MiB x 2")
         del src, dst
 
-    b = config_batch(1)
+    b = config_batch(args.workload)
     log(f"workload {b.name}: R={b.num_reqs} T={b.total_q} context tokens={int(b.context_lens.sum())}")
     dev = DeviceBatch(b)
     ms, trace = time_steps(dev.step, args.steps, args.warmup)

@@ -128,6 +128,54 @@ bool matrix_ok(const pensieve_batch_desc* d) {
   return G >= 1 && G <= 32 && (32 % G) == 0;
 }
 
+// Workgroup i of a launch runs on XCD i % kXcds, and each XCD has its own L2.
+// Matrix-core items of one (request, KV head, partition) stream the same K/V,
+// so they are kept on one XCD: such groups are spread over kXcds bins by cost
+// (largest group first into the lightest bin), each bin lists its items longest
+// first, and the bins are interleaved so that bin x occupies launch slots
+// x, x + kXcds, ...  Bins are padded to equal length with zero-row items, which
+// the kernel leaves at once.
+constexpr int kXcds = 8;
+
+std::vector<PlannedItem> xcd_order(std::vector<PlannedItem> items) {
+  if (items.size() < 2 * kXcds) return items;
+  struct Group { long long cost = 0; std::vector<PlannedItem> items; };
+  std::vector<Group> groups;
+  std::unordered_map<long long, size_t> index;
+  for (const PlannedItem& p : items) {
+    const long long k = ((long long)p.w.req * 65536 + p.w.kv_head) * 1024 + p.w.part;
+    auto it = index.find(k);
+    if (it == index.end()) {
+      index[k] = groups.size();
+      groups.push_back({});
+      it = index.find(k);
+    }
+    groups[it->second].cost += p.cost;
+    groups[it->second].items.push_back(p);
+  }
+  std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.cost > b.cost; });
+  std::vector<std::vector<PlannedItem>> bins(kXcds);
+  std::vector<long long> load(kXcds, 0);
+  for (Group& g : groups) {
+    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    load[x] += g.cost;
+    bins[x].insert(bins[x].end(), g.items.begin(), g.items.end());
+  }
+  size_t longest = 0;
+  for (auto& b : bins) {
+    std::stable_sort(b.begin(), b.end(), [](const PlannedItem& a, const PlannedItem& c) { return a.cost > c.cost; });
+    longest = std::max(longest, b.size());
+  }
+  std::vector<PlannedItem> out;
+  out.reserve(longest * kXcds);
+  PlannedItem filler = items.front();
+  filler.w.q_count = 0;
+  filler.cost = 0;
+  for (size_t k = 0; k < longest; ++k)
+    for (int x = 0; x < kXcds; ++x) out.push_back(k < bins[x].size() ? bins[x][k] : filler);
+  return out;
+}
+
 void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
   const int G = d->num_heads / d->num_kv_heads;
   const bool mat = matrix_ok(d);
@@ -178,14 +226,18 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
     if (key(a) != key(b)) return key(a) < key(b);
     return a.cost > b.cost;
   });
+  size_t nmat = 0;
+  while (nmat < all.size() && all[nmat].kernel == kMatrix) ++nmat;
+  std::vector<PlannedItem> ordered = xcd_order(std::vector<PlannedItem>(all.begin(), all.begin() + nmat));
+  ordered.insert(ordered.end(), all.begin() + nmat, all.end());
   plan.items.clear();
   plan.segments.clear();
-  plan.planned = all;
-  for (size_t i = 0; i < all.size(); ++i) {
-    plan.items.push_back(all[i].w);
-    if (plan.segments.empty() || plan.segments.back().kernel != all[i].kernel ||
-        plan.segments.back().param != all[i].param) {
-      plan.segments.push_back({all[i].kernel, all[i].param, (int)i, 0});
+  plan.planned = ordered;
+  for (size_t i = 0; i < ordered.size(); ++i) {
+    plan.items.push_back(ordered[i].w);
+    if (plan.segments.empty() || plan.segments.back().kernel != ordered[i].kernel ||
+        plan.segments.back().param != ordered[i].param) {
+      plan.segments.push_back({ordered[i].kernel, ordered[i].param, (int)i, 0});
     }
     plan.segments.back().count++;
   }
@@ -295,21 +347,82 @@ struct TraceScope {
   }
 };
 
+// Side stream and fork/join events per device: when a plan has both
+// matrix-core and vector items, the vector segments run on the side stream
+// concurrently with the matrix-core segment (they touch disjoint requests and
+// outputs), and the caller's stream waits for both.
+struct Concurrency {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_conc_mu;
+std::unordered_map<int, Concurrency> g_conc;
+
+hipError_t concurrency_for_current_device(Concurrency** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_conc_mu);
+  Concurrency& c = g_conc[dev];
+  if (!c.side) {
+    if ((e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &c;
+  return hipSuccess;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev] = n;
+  return n;
+}
+
 pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::AttnArgs& args, void* workspace,
                          hipStream_t stream) {
   hipError_t e = stage_to_device(workspace, plan.items.data(), plan.items.size() * sizeof(pk::WorkItem), stream);
   if (e != hipSuccess) return hip_fail(e, "work-list upload");
   const pk::WorkItem* dev_items = static_cast<const pk::WorkItem*>(workspace);
+  bool has_matrix = false, has_vector = false;
+  for (const Segment& s : plan.segments) (s.kernel == kMatrix ? has_matrix : has_vector) = true;
+  Concurrency* conc = nullptr;
+  // Overlap only when the matrix-core items alone cannot occupy every CU
+  // (two workgroups per CU); otherwise the kernels just contend for CUs.
+  int matrix_items = 0;
+  for (const Segment& s : plan.segments)
+    if (s.kernel == kMatrix) matrix_items += s.count;
+  const bool fork = has_matrix && has_vector && matrix_items < 2 * device_cu_count();
+  std::unique_lock<std::mutex> side_lock;
+  if (fork) {
+    if ((e = concurrency_for_current_device(&conc)) != hipSuccess) return hip_fail(e, "side stream");
+    side_lock = std::unique_lock<std::mutex>(g_conc_mu);   // one fork/join at a time per process
+    if ((e = hipEventRecord(conc->fork, stream)) != hipSuccess) return hip_fail(e, "fork event");
+    if ((e = hipStreamWaitEvent(conc->side, conc->fork, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+  }
   for (const Segment& s : plan.segments) {
     pk::AttnArgs a = args;
     a.items = dev_items + s.begin;
     a.num_items = s.count;
-    TraceScope trace(s.kernel == kMatrix ? kTraceMatrix : kTraceVector, s.count, stream);
+    const hipStream_t st = (fork && s.kernel == kVector) ? conc->side : stream;
+    TraceScope trace(s.kernel == kMatrix ? kTraceMatrix : kTraceVector, s.count, st);
     if (s.kernel == kMatrix)
-      e = pk::launch_attn_mfma(a, d->dtype, d->head_dim, s.param, stream);
+      e = pk::launch_attn_mfma(a, d->dtype, d->head_dim, s.param, st);
     else
-      e = pk::launch_attn_vector(a, d->dtype, d->head_dim, s.param, stream);
+      e = pk::launch_attn_vector(a, d->dtype, d->head_dim, s.param, st);
     if (e != hipSuccess) return hip_fail(e, s.kernel == kMatrix ? "matrix-core attention launch" : "vector attention launch");
+  }
+  if (fork) {
+    if ((e = hipEventRecord(conc->join, conc->side)) != hipSuccess) return hip_fail(e, "join event");
+    if ((e = hipStreamWaitEvent(stream, conc->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
   }
   return ok();
 }

@@ -39,6 +39,11 @@ struct Mfma<kF16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ _Float16 cvt(float x) { return (_Float16)x; }
+  static __device__ __forceinline__ float dot2_ones(_Float16 a, _Float16 b, float acc) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 ab = {a, b}, one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(ab, one, acc, false);
+  }
 };
 
 template <>
@@ -48,6 +53,11 @@ struct Mfma<kBF16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ __bf16 cvt(float x) { return (__bf16)x; }
+  static __device__ __forceinline__ float dot2_ones(__bf16 a, __bf16 b, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ab = {a, b}, one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(ab, one, acc, false);
+  }
 };
 
 __device__ __forceinline__ int wave_max_i(int x) {
@@ -73,26 +83,80 @@ __device__ __forceinline__ u32x4 zero_keys_from(u32x4 v, int first, int limit) {
   return v;
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most N vector-memory operations are outstanding, or
+// until every LDS / scalar-memory operation has finished.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+constexpr int lgkmcnt0_imm() { return 63 | (3 << 14) | (7 << 4); }
+
+// 16 bytes per lane from `base + voff` (a buffer resource of `nbytes` bytes: offsets past
+// it read as zero) straight into LDS at `lds_dst + 16 * lane`.  Issued as inline assembly
+// so that the compiler's wait-count tracking, which cannot tell one LDS stage from another,
+// does not wait for these loads before every LDS read; callers wait for them explicitly
+// with s_waitcnt vmcnt.  M0 carries the LDS address; nothing else in these kernels uses M0.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t nbytes, uint32_t voff, uint8_t* lds_dst) {
+  const unsigned long long b = (unsigned long long)base;
+  const i32x4 rsrc = {(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)nbytes, kBufferWord3};
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(m0)
+               : "memory");
+}
+
+// Workgroup barrier that does not wait for outstanding memory operations (LDS-DMA
+// loads of later tiles stay in flight); the wavefront-scope fences only keep the
+// compiler from moving memory accesses across it.  Callers wait explicitly for
+// what must be complete.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Max of x over lanes l and l ^ 32 (v_permlane32_swap moves the two halves past each other).
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)pr[0]), __builtin_bit_cast(float, (int)pr[1]));
+}
+
+// V tiles keep the pool layout in LDS ([16 keys] per dim row, 32 bytes); the two 16-byte
+// halves of dim row d trade places when vswz(d) = 1, so that the 8 or 16 lanes reading one
+// half column from consecutive dim rows hit distinct bank groups.
+__device__ __forceinline__ int vswz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+
+// XOR swizzle of the 16-byte chunk slots of K row r in LDS: chunk c of row r
+// lives in slot c ^ kswz(r).  kswz swaps bits 2 and 3 of r (mod 16), the same
+// permutation the MFMA row order uses, so the 8 or 16 lanes that read one
+// chunk column from 8 or 16 different rows hit distinct bank groups.
+template <int KCH>
+__device__ __forceinline__ int kswz_rows(int r) {
+  const int x = r & 15;
+  return ((x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1)) & (KCH - 1);
+}
+
 template <int DT, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   using MM = Mfma<DT>;
   using vec8 = typename MM::vec8;
-  constexpr int KS = D / 16;           // k-steps of K.Q^T
-  constexpr int MBD = D / 32;          // 32-dim blocks of O^T
-  constexpr int KT = 64;               // keys per tile
-  constexpr int TOKW = 32 / G;         // tokens per wave
-  constexpr int KROW = D * 2 + 16;     // LDS bytes per K row (padded)
-  constexpr int VROW = KT * 2 + 16;    // LDS bytes per V^T dim row (padded)
-  constexpr int KBYTES = KT * KROW;
-  constexpr int VBYTES = D * VROW;
-  constexpr int OROW = D * 4 + 16;     // epilogue: fp32 output row
+  constexpr int KS = D / 16;              // k-steps of K.Q^T
+  constexpr int MBD = D / 32;             // 32-dim blocks of O^T
+  constexpr int KT = 64;                  // keys per tile (four blocks)
+  constexpr int TOKW = 32 / G;            // tokens per wave
+  constexpr int BLK = 16 * D * 2;         // bytes of one block's K (or V) tile
+  constexpr int STAGE = 4 * BLK;          // one 64-key tile of K (or V)
+  constexpr int NI = BLK / 1024;          // 1 KB LDS-DMA loads per block and tensor
+  constexpr int KCH = D / 8;              // 16-byte chunks per K row
+  constexpr int RPI = 1024 / (2 * D);     // K rows per DMA load
+  constexpr int OROW = D * 4 + 16;        // epilogue: fp32 output row
   constexpr int OBYTES = 128 * OROW;
-  constexpr int LDS_BYTES = (KBYTES + VBYTES) > OBYTES ? (KBYTES + VBYTES) : OBYTES;
-  constexpr int CB = 2 * D;            // 16-byte chunks per block tile
-  constexpr int CPT = 4 * CB / 256;    // chunks per thread per tile (per tensor)
-  constexpr int KCH = D / 8;           // 16-byte chunks per K row
-  constexpr size_t TILE = (size_t)16 * D * 2;
+  constexpr int PIPE = 4 * STAGE;         // K stages 0,1 then V stages 0,1
+  constexpr int LDS_BYTES = PIPE > OBYTES ? PIPE : OBYTES;
   static_assert(G >= 1 && G <= 32 && (32 % G) == 0, "group size must divide 32");
+  static_assert(NI >= 1, "a block tile must fill whole 1 KB loads");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int s_wmax[4];
@@ -103,14 +167,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   const int h2 = lane >> 5;
   const int n = lane & 31;
   const WorkItem it = a.items[blockIdx.x];
+  if (it.q_count == 0) return;   // filler item (whole workgroup leaves before any barrier)
   const int r = it.req, g = it.kv_head;
   const int Hq = a.num_heads, Hkv = a.num_kv_heads;
   const int L = a.context_lens[r];
   const int row0 = a.cu_q_lens[r];
   const int q_r = a.cu_q_lens[r + 1] - row0;
   const float c = a.scale_log2;
+  constexpr float kSlack = 8.0f;          // log2 headroom before the running max must move
+  const float slack_raw = kSlack / c;
 
-  // ---- this lane's query row ----------------------------------------------------
+  // ---- this lane's query row --------------------------------------------------------------
   const int tok = w * TOKW + n / G;
   const bool row_valid = tok < it.q_count;
   const size_t qrow = (size_t)row0 + it.q_begin + (row_valid ? tok : 0);
@@ -131,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   __syncthreads();
   const int pmax_wg = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
 
-  // ---- key range of this item ------------------------------------------------------
+  // ---- key range of this item ----------------------------------------------------------------
   const int nblk = (L + 15) >> 4;
   const int per = (nblk + it.num_parts - 1) / it.num_parts;
   const int kb0 = it.part * per;
@@ -141,123 +208,164 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   const int t_end = min(t_valid, pmax_wg + 1);
   const int ntiles = (t_end > t_begin) ? (t_end - t_begin + KT - 1) / KT : 0;
 
-  const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
-  u32x4 kst[CPT], vst[CPT];
-  auto load_tile = [&](int t0) {
-    const int blk0 = t0 >> 4;
+  // ---- LDS-DMA tile loads ---------------------------------------------------------------------
+  // Wave w loads block w of each tile, K and V, with NI buffer loads of 1 KB each straight into
+  // LDS (lane l lands at +16 l).  K stage: row t (0..63) at t * 2D, chunk c in slot c ^ kswz(t).
+  // V stage: block b at b * BLK as [D][16]; the two 16-byte halves of dim row d are swapped when
+  // vswz(d) is set.  Source offsets inside a block tile depend only on the lane: computed once.
+  const const_i32_ptr bt = as_const(a.block_tables) + (size_t)r * a.bt_stride;
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int wbase = w * 64 + 256 * x;       // first chunk of this wave's load
-      const int b = wbase / CB;                 // block within the tile (wave-uniform)
-      const int ch = (wbase % CB) + lane;
-      int lb = blk0 + b;
-      lb = (lb < kb1) ? lb : kb0;               // past the partition: any block of it (masked)
-      const size_t off = ((size_t)bt[lb] * Hkv + g) * TILE + (size_t)ch * 16;
-      kst[x] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
-      vst[x] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
-    }
+  for (int j = 0; j < NI; ++j) {
+    const int t16 = j * RPI + lane / KCH;
+    koff[j] = (uint32_t)(t16 * 2 * D + ((lane % KCH) ^ kswz_rows<KCH>(t16)) * 16);
+    const int d = j * 32 + lane / 2;
+    voff[j] = (uint32_t)(d * 32 + ((lane & 1) ^ vswz(d)) * 16);
+  }
+  auto block_of = [&](int tile) {            // physical block loaded by this wave for `tile`
+    int lb = kb0 + 4 * tile + w;
+    lb = (lb < kb1) ? lb : kb0;              // past the partition: any block of it (masked)
+    return bt[lb];
   };
-  auto write_tile = [&](int t0) {
-    const bool tail = t0 + KT > t_valid;
+  auto issue = [&](const uint8_t* pool, const uint32_t* offs, int tile, uint8_t* stage) {
+    const uint8_t* src = pool + ((size_t)block_of(tile) * Hkv + g) * BLK;
 #pragma unroll
-    for (int x = 0; x < CPT; ++x) {
-      const int wbase = w * 64 + 256 * x;
-      const int b = wbase / CB;
-      const int ch = (wbase % CB) + lane;
-      const int krow = b * 16 + ch / KCH, kcol = ch % KCH;
-      const int vd = ch >> 1, vh = ch & 1;
-      u32x4 kv = kst[x], vv = vst[x];
-      if (tail) {
-        if (t0 + krow >= t_valid) kv = u32x4{0, 0, 0, 0};
-        vv = zero_keys_from(vv, t0 + b * 16 + vh * 8, t_valid);
-      }
-      *reinterpret_cast<u32x4*>(lds + krow * KROW + kcol * 16) = kv;
-      *reinterpret_cast<u32x4*>(lds + KBYTES + vd * VROW + (b * 16 + vh * 8) * 2) = vv;
-    }
+    for (int j = 0; j < NI; ++j) lds_dma16(src, BLK, offs[j], stage + w * BLK + j * 1024);
   };
+  auto kstage = [&](int tile) { return lds + (tile & 1) * STAGE; };
+  auto vstage = [&](int tile) { return lds + (2 + (tile & 1)) * STAGE; };
 
   float m_run = -INFINITY, l_run = 0.f;
+  float m_top = -INFINITY;                   // true running max (m_run may lag it by up to the slack)
   f32x16 acc[MBD];
 #pragma unroll
   for (int j = 0; j < MBD; ++j) acc[j] = f32x16{};
   // LDS row of the K key that MFMA row (32 mb + n) multiplies: bits 2 and 3 swapped.
   const int krow_of_n = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
+  // S^T of one tile for this lane's row: s[mb][v] is key t0 + 32 mb + 16 (v / 8) + 8 h2 + v % 8.
+  auto qk = [&](int tile, f32x16* sc) {
+    const uint8_t* ks_base = kstage(tile);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      sc[mb] = f32x16{};
+      const uint8_t* kp = ks_base + (32 * mb + krow_of_n) * (2 * D);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = (2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n);
+        const vec8 kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(kp + slot * 16));
+        sc[mb] = MM::mma(kop, qreg[ks], sc[mb]);
+      }
+    }
+  };
+
+  f32x16 s_cur[2], s_nxt[2];
+  wait_vmem_all();                           // query rows and positions have landed
   if (ntiles > 0) {
-    load_tile(t_begin);
-    write_tile(t_begin);
+    issue(a.k_pool, koff, 0, kstage(0));
+    if (ntiles > 1) issue(a.k_pool, koff, 1, kstage(1));
+    issue(a.v_pool, voff, 0, vstage(0));
+    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
+    lds_barrier();
+    if (t_begin <= pmax_w) qk(0, s_cur);
   }
-  __syncthreads();
+
   for (int ti = 0; ti < ntiles; ++ti) {
     const int t0 = t_begin + ti * KT;
-    const bool more = ti + 1 < ntiles;
-    if (more) load_tile(t0 + KT);
-    if (t0 <= pmax_w) {
-      f32x16 s[2];
+    const bool k2 = ti + 2 < ntiles, v1 = ti + 1 < ntiles;
+    __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+    lds_barrier();            // every wave is done with QK(ti) and PV(ti - 1)
+    if (k2) issue(a.k_pool, koff, ti + 2, kstage(ti + 2));
+    if (v1) issue(a.v_pool, voff, ti + 1, vstage(ti + 1));
+    if (k2) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
+    else if (v1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    lds_barrier();            // K(ti + 1) and V(ti) are in LDS
+    if (t0 + KT > t_valid) {
+      // Tail: keys at or past t_valid must contribute exactly 0; stale V may hold NaN.
+      uint8_t* vs = vstage(ti);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-        const uint8_t* kp = lds + (32 * mb + krow_of_n) * KROW + h2 * 16;
+      for (int x = 0; x < 2; ++x) {
+        const int row = tid + 256 * x;       // (block, dim row) pairs: 4 x D
+        if (row < 4 * D) {
+          const int b = row / D, d = row % D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const vec8 kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(kp + ks * 32));
-          s[mb] = MM::mma(kop, qreg[ks], s[mb]);
+          for (int hh = 0; hh < 2; ++hh) {
+            u32x4* p = reinterpret_cast<u32x4*>(vs + b * BLK + d * 32 + ((hh ^ vswz(d)) * 16));
+            *p = zero_keys_from(*p, t0 + 16 * b + 8 * hh, t_valid);
+          }
         }
       }
-      // s[mb][v] is the score of key t0 + 32 mb + 16 (v / 8) + 8 h2 + v % 8 for this lane's row.
+      __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+      lds_barrier();
+    }
+    const bool next_live = v1 && (t0 + KT <= pmax_w);
+    if (next_live) qk(ti + 1, s_nxt);
+    if (t0 <= pmax_w) {
       if ((t0 + KT - 1 > pmin_w) || (t0 + KT > t_valid)) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int tk = t0 + 32 * mb + 16 * (v >> 3) + 8 * h2 + (v & 7);
-            s[mb][v] = (tk <= pos && tk < t_valid) ? s[mb][v] : -INFINITY;
+            s_cur[mb][v] = (tk <= pos && tk < t_valid) ? s_cur[mb][v] : -INFINITY;
           }
       }
-      float mx = s[0][0];
+      // Row max over the 32 scores of this lane, then with the lane holding the other 32 keys.
+      float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s_cur[0][v]), s_cur[0][v + 1]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = fast_exp2((m_run - m_use) * c);
-      const float mc = m_use * c;
-      float ls = 0.f;
+      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s_cur[1][v]), s_cur[1][v + 1]);
+      mx = half_swap_max(mx);
+      m_top = fmaxf(m_top, mx);
+      // The running max moves only when some row's tile max exceeds it by more than
+      // kSlack / c (raw score units); otherwise weights stay <= 2^kSlack and the
+      // accumulator needs no rescale.  Any row's growth moves all rows of the wave.
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + slack_raw) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = fast_exp2((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+        l_run *= corr;
+#pragma unroll
+        for (int j = 0; j < MBD; ++j) acc[j] *= corr;
+        m_run = m_new;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
       vec8 pb[4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(fmaf(s[mb][v], c, -mc));
-          ls += p;
-          pb[2 * mb + (v >> 3)][v & 7] = MM::cvt(p);
-        }
-      l_run = fmaf(l_run, corr, ls);
-      m_run = m_new;
+        for (int v = 0; v < 16; ++v) pb[2 * mb + (v >> 3)][v & 7] = MM::cvt(fast_exp2(fmaf(s_cur[mb][v], c, -mc)));
+      // Row sum of the rounded weights (the same values the P.V product uses).
 #pragma unroll
-      for (int j = 0; j < MBD; ++j) acc[j] *= corr;
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) l_run = MM::dot2_ones(pb[ks][e], pb[ks][e + 1], l_run);
+      // O^T += V^T P^T: k-step ks is block ks of the tile.
+      const uint8_t* vs = vstage(ti);
 #pragma unroll
       for (int j = 0; j < MBD; ++j) {
-        const uint8_t* vp = lds + KBYTES + (32 * j + n) * VROW + h2 * 16;
+        const int d = 32 * j + n;
+        const uint8_t* vp = vs + d * 32 + ((h2 ^ vswz(d)) * 16);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const vec8 vop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(vp + ks * 32));
+          const vec8 vop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(vp + ks * BLK));
           acc[j] = MM::mma(vop, pb[ks], acc[j]);
         }
       }
     }
-    __syncthreads();
-    if (more) {
-      write_tile(t0 + KT);
-      __syncthreads();
+    if (next_live) {
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
     }
   }
 
-  // ---- epilogue: normalise, stage rows in LDS, store coalesced -----------------------
+  // ---- epilogue: normalise, stage rows in LDS, store coalesced -----------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
+  __syncthreads();                            // every wave is done reading the pipeline stages
   {
     uint8_t* orow = lds + (w * 32 + n) * OROW;
 #pragma unroll
@@ -271,9 +379,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   }
   const bool split = a.write_partials || it.num_parts > 1;
   if (split && h2 == 0 && row_valid) {
+    // Report l relative to the true max: l_top = l_tot * exp2((m_run - m_top) c).
     const size_t pi = (qrow * Hq + h) * a.part_stride + it.part;
-    a.part_m[pi] = (m_run == -INFINITY) ? -INFINITY : m_run * a.scale;
-    a.part_l[pi] = l_tot;
+    const bool any = m_top != -INFINITY;
+    a.part_m[pi] = any ? m_top * a.scale : -INFINITY;
+    a.part_l[pi] = any ? l_tot * fast_exp2((m_run - m_top) * c) : 0.f;
   }
   __syncthreads();
   if (!split) {

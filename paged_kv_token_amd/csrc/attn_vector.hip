@@ -91,15 +91,15 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
     for (int j = 0; j < VI; ++j) acc[n][j] = 0.f;
   }
 
-  const int32_t* bt = a.block_tables + (size_t)r * a.bt_stride;
+  const const_i32_ptr bt = as_const(a.block_tables) + (size_t)r * a.bt_stride;
   auto load = [&](int blk, u32x4* kr, u32x4* vr) {
-    const int phys = bt[blk];
+    const int phys = bt[uniform(blk)];
     const uint8_t* kt = a.k_pool + ((size_t)phys * Hkv + g) * TILE;
     const uint8_t* vt = a.v_pool + ((size_t)phys * Hkv + g) * TILE;
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kt + (size_t)(i * 64 + lane) * 16);
+    for (int i = 0; i < KI; ++i) kr[i] = tile_load16(kt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
 #pragma unroll
-    for (int j = 0; j < VI; ++j) vr[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)(j * 64 + lane) * 16);
+    for (int j = 0; j < VI; ++j) vr[j] = tile_load16(vt, (uint32_t)TILE, (uint32_t)(j * 64 + lane) * 16u);
   };
 
   auto process = [&](int blk, const u32x4* kr, const u32x4* vr) {
@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   {
     u32x4 kc[KI], vc[VI];
     int blk = kb0 + w;
+    wait_vmem_all();
     if (blk < kb1) load(blk, kc, vc);
     for (; blk < kb1; blk += NW) {
       u32x4 kn[KI] = {}, vn[VI] = {};

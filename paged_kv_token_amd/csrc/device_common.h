@@ -154,6 +154,32 @@ __device__ __forceinline__ float xor_sum_from(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load of chunk `off` (bytes) of a tile through a buffer resource whose
+// base is the wave-uniform tile address.  The offset VGPR is the only per-lane
+// operand, so no 64-bit per-tile address is formed in VGPRs, and offsets at or
+// beyond tile_bytes read as zero.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ u32x4 tile_load16(const uint8_t* tile, uint32_t tile_bytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tile), (short)0, (int)tile_bytes, kBufferWord3);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Block tables, lengths and work items are never written by a kernel that
+// reads them; reading them through the constant address space lets uniform
+// reads become scalar loads, which count on lgkmcnt instead of the in-order
+// vector-memory counter that tracks the K/V stream.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ const_i32_ptr as_const(const int32_t* p) { return (const_i32_ptr)p; }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum).  Placed once
+// before a streaming loop: the compiler's wait-count tracking cannot prove at
+// the loop header that loads issued before the loop (query rows, positions)
+// have landed, and would otherwise wait on the vector-memory counter inside
+// every iteration -- which, the counter being in order, also waits for the
+// prefetch just issued for the next tile.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace pk

@@ -98,10 +98,19 @@ def test_plan_covers_each_row_head_once(lib, index):
     b = config_batch(index)
     plan = pk.pensieve_debug_plan(desc_for(b))
     assert np.all(_coverage(b, plan) == 1)
-    # longest first inside each kernel segment
-    for k in (0, 1):
-        costs = [row[7] for row in plan if row[0] == k]
-        assert costs == sorted(costs, reverse=True) or k == 0   # vector items are grouped by width first
+    mat = plan[plan[:, 0] == 1]
+    if len(mat) >= 16:
+        # matrix-core items: interleaved over 8 XCD bins (slot % 8); each bin runs longest first and
+        # keeps all items of one (request, KV head, partition) together
+        assert len(mat) % 8 == 0
+        owner = {}
+        for x in range(8):
+            live = [row for row in mat[x::8] if row[4] > 0]
+            costs = [row[7] for row in live]
+            assert costs == sorted(costs, reverse=True)
+            for row in live:
+                assert owner.setdefault((row[1], row[2], row[5]), x) == x
+        assert np.all(mat[mat[:, 4] == 0][:, 7] == 0)    # fillers carry no work
 
 
 @pytest.mark.parametrize("P", [1, 7, 32])
