@@ -22,6 +22,8 @@
 // consecutive keys, which is exactly the layout of the P^T operand, and the
 // V^T operand is one 16-byte LDS read of 8 consecutive keys of one dim row
 // (the V pool stores each block as [D][16], so V^T needs no transpose).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -243,19 +245,34 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // LDS row of the K key that MFMA row (32 mb + n) multiplies: bits 2 and 3 swapped.
   const int krow_of_n = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
+  // Per-lane LDS read offsets, fixed for the whole item.  K: row (32 mb + krow_of_n) and
+  // chunk (2 ks + h2) live at krd[ks] + 64 D mb inside a K stage.  V: dim row 32 j + n, half
+  // h2 of block ks lives at vrd + 1024 j + BLK ks inside a V stage (vswz(32 j + n) = vswz(n)).
+  uint32_t krd[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    krd[ks] = (uint32_t)(krow_of_n * 2 * D + (((2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n)) * 16));
+  const uint32_t vrd = (uint32_t)(n * 32 + ((h2 ^ vswz(n)) * 16));
+
   // S^T of one tile for this lane's row: s[mb][v] is key t0 + 32 mb + 16 (v / 8) + 8 h2 + v % 8.
-  auto qk = [&](int tile, f32x16* sc) {
-    const uint8_t* ks_base = kstage(tile);
+  // K operands are read in batches of four k-steps for both 32-key halves, and the two
+  // independent accumulator chains alternate, so LDS latency overlaps the MFMAs.
+  auto qk = [&](const uint8_t* ks_base, f32x16* sc) {
+    sc[0] = f32x16{};
+    sc[1] = f32x16{};
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      sc[mb] = f32x16{};
-      const uint8_t* kp = ks_base + (32 * mb + krow_of_n) * (2 * D);
+    for (int k0 = 0; k0 < KS; k0 += 4) {
+      vec8 kop[4][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int slot = (2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n);
-        const vec8 kop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(kp + slot * 16));
-        sc[mb] = MM::mma(kop, qreg[ks], sc[mb]);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          kop[kk][mb] = __builtin_bit_cast(
+              vec8, *reinterpret_cast<const u32x4*>(ks_base + krd[k0 + kk] + mb * 64 * D));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) sc[mb] = MM::mma(kop[kk][mb], qreg[k0 + kk], sc[mb]);
     }
   };
 
@@ -268,23 +285,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
     lds_barrier();
-    if (t_begin <= pmax_w) qk(0, s_cur);
+    qk(lds, s_cur);
   }
 
-  for (int ti = 0; ti < ntiles; ++ti) {
+  // One tile: PAR is ti & 1 (the K stage of tile ti + 1 and the V stage of tile ti are
+  // compile-time offsets); s_cur holds S^T of tile ti, s_nxt receives S^T of tile ti + 1.
+  auto tile_step = [&](int ti, auto par, f32x16* s_cur, f32x16* s_nxt) {
+    constexpr int PAR = decltype(par)::value;
+    uint8_t* const k_next = lds + (1 - PAR) * STAGE;     // K stage of tile ti + 1
+    uint8_t* const k_free = lds + PAR * STAGE;           // K stage of tile ti (free after QK(ti))
+    uint8_t* const v_cur = lds + (2 + PAR) * STAGE;      // V stage of tile ti
+    uint8_t* const v_free = lds + (3 - PAR) * STAGE;     // V stage of tile ti - 1
     const int t0 = t_begin + ti * KT;
     const bool k2 = ti + 2 < ntiles, v1 = ti + 1 < ntiles;
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
-    lds_barrier();            // every wave is done with QK(ti) and PV(ti - 1)
-    if (k2) issue(a.k_pool, koff, ti + 2, kstage(ti + 2));
-    if (v1) issue(a.v_pool, voff, ti + 1, vstage(ti + 1));
+    lds_barrier();                            // every wave is done with QK(ti) and PV(ti - 1)
+    if (k2) issue(a.k_pool, koff, ti + 2, k_free);
+    if (v1) issue(a.v_pool, voff, ti + 1, v_free);
     if (k2) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
     else if (v1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-    lds_barrier();            // K(ti + 1) and V(ti) are in LDS
+    lds_barrier();                            // K(ti + 1) and V(ti) are in LDS
     if (t0 + KT > t_valid) {
       // Tail: keys at or past t_valid must contribute exactly 0; stale V may hold NaN.
-      uint8_t* vs = vstage(ti);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int row = tid + 256 * x;       // (block, dim row) pairs: 4 x D
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
           const int b = row / D, d = row % D;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            u32x4* p = reinterpret_cast<u32x4*>(vs + b * BLK + d * 32 + ((hh ^ vswz(d)) * 16));
+            u32x4* p = reinterpret_cast<u32x4*>(v_cur + b * BLK + d * 32 + ((hh ^ vswz(d)) * 16));
             *p = zero_keys_from(*p, t0 + 16 * b + 8 * hh, t_valid);
           }
         }
@@ -300,65 +323,70 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
       lds_barrier();
     }
-    const bool next_live = v1 && (t0 + KT <= pmax_w);
-    if (next_live) qk(ti + 1, s_nxt);
-    if (t0 <= pmax_w) {
-      if ((t0 + KT - 1 > pmin_w) || (t0 + KT > t_valid)) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int tk = t0 + 32 * mb + 16 * (v >> 3) + 8 * h2 + (v & 7);
-            s_cur[mb][v] = (tk <= pos && tk < t_valid) ? s_cur[mb][v] : -INFINITY;
-          }
-      }
-      // Row max over the 32 scores of this lane, then with the lane holding the other 32 keys.
-      float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
-#pragma unroll
-      for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s_cur[0][v]), s_cur[0][v + 1]);
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s_cur[1][v]), s_cur[1][v + 1]);
-      mx = half_swap_max(mx);
-      m_top = fmaxf(m_top, mx);
-      // The running max moves only when some row's tile max exceeds it by more than
-      // kSlack / c (raw score units); otherwise weights stay <= 2^kSlack and the
-      // accumulator needs no rescale.  Any row's growth moves all rows of the wave.
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + slack_raw) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = fast_exp2((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
-        l_run *= corr;
-#pragma unroll
-        for (int j = 0; j < MBD; ++j) acc[j] *= corr;
-        m_run = m_new;
-      }
-      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-      vec8 pb[4];
+    // Masking (diagonal and tail tiles only): key offset 32 mb + 16 (v / 8) + v % 8 from
+    // t0 + 8 h2 is visible iff it is <= lim.
+    if ((t0 + KT - 1 > pmin_w) || (t0 + KT > t_valid)) {
+      const int lim = min(pos, t_valid - 1) - (t0 + 8 * h2);
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) pb[2 * mb + (v >> 3)][v & 7] = MM::cvt(fast_exp2(fmaf(s_cur[mb][v], c, -mc)));
-      // Row sum of the rounded weights (the same values the P.V product uses).
+        for (int v = 0; v < 16; ++v)
+          s_cur[mb][v] = (32 * mb + 16 * (v >> 3) + (v & 7) <= lim) ? s_cur[mb][v] : -INFINITY;
+    }
+    // Row max over the 32 scores of this lane, then with the lane holding the other 32 keys.
+    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+#pragma unroll
+    for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s_cur[0][v]), s_cur[0][v + 1]);
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s_cur[1][v]), s_cur[1][v + 1]);
+    mx = half_swap_max(mx);
+    m_top = fmaxf(m_top, mx);
+    // The running max moves only when some row's tile max exceeds it by more than
+    // kSlack / c (raw score units); otherwise weights stay <= 2^kSlack and the
+    // accumulator needs no rescale.  Any row's growth moves all rows of the wave.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + slack_raw) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);
+      l_run *= corr;
+#pragma unroll
+      for (int j = 0; j < MBD; ++j) acc[j] *= corr;
+      m_run = m_new;
+    }
+    // One straight-line region: QK of the next tile (independent MFMAs), the weights of
+    // this tile (VALU), then O^T += V^T P^T.  The next tile's QK is computed even when it
+    // does not exist (its result is then never read), so that no branch splits the region
+    // and the scheduler can interleave the MFMAs with the exponentials.
+    qk(k_next, s_nxt);
+    const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+    vec8 pb[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) pb[2 * mb + (v >> 3)][v & 7] = MM::cvt(fast_exp2(fmaf(s_cur[mb][v], c, -mc)));
+    // Row sum of the rounded weights (the same values the P.V product uses).
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) l_run = MM::dot2_ones(pb[ks][e], pb[ks][e + 1], l_run);
+    // O^T += V^T P^T: k-step ks is block ks of the tile.
+#pragma unroll
+    for (int j0 = 0; j0 < MBD; j0 += 2) {
+      vec8 vop[2][4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          vop[jj][ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(v_cur + vrd + (j0 + jj) * 1024 + ks * BLK));
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) l_run = MM::dot2_ones(pb[ks][e], pb[ks][e + 1], l_run);
-      // O^T += V^T P^T: k-step ks is block ks of the tile.
-      const uint8_t* vs = vstage(ti);
-#pragma unroll
-      for (int j = 0; j < MBD; ++j) {
-        const int d = 32 * j + n;
-        const uint8_t* vp = vs + d * 32 + ((h2 ^ vswz(d)) * 16);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const vec8 vop = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(vp + ks * BLK));
-          acc[j] = MM::mma(vop, pb[ks], acc[j]);
-        }
-      }
+        for (int jj = 0; jj < 2; ++jj) acc[j0 + jj] = MM::mma(vop[jj][ks], pb[ks], acc[j0 + jj]);
     }
-    if (next_live) {
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
-    }
+  };
+
+  for (int ti = 0; ti < ntiles; ti += 2) {
+    tile_step(ti, std::integral_constant<int, 0>{}, s_cur, s_nxt);
+    if (ti + 1 < ntiles) tile_step(ti + 1, std::integral_constant<int, 1>{}, s_nxt, s_cur);
   }
 
   // ---- epilogue: normalise, stage rows in LDS, store coalesced -----------------------------------
