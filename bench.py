@@ -134,19 +134,33 @@ def request_bytes(b, r: int) -> int:
     return kv + qo + meta
 
 
-def request_flops(b, r: int) -> int:
-    """QK^T and PV over visible (row, key) pairs only: 4 d Hq (p + 1) per row."""
-    pos = b.query_positions(r)
-    return int(4 * b.head_dim * b.num_heads * int((pos + 1).sum()))
+PLAN_KERNELS = {0: "attn_vector", 1: "attn_mfma"}
 
 
-def kernel_requests(dev: DeviceBatch, num_partitions: int = 0):
-    """Requests served by each attention kernel (from the library's own plan)."""
-    plan = pk.pensieve_debug_plan(dev.desc, num_partitions)
-    out = {"attn_vector": set(), "attn_mfma": set()}
-    for row in plan:
-        out["attn_mfma" if row[0] == 1 else "attn_vector"].add(int(row[1]))
-    return out
+def kernel_work(dev: DeviceBatch, kernel: str):
+    """Algorithmic (bytes, flops) of the items one attention kernel serves, from the library's own plan.
+
+    Bytes: each (request, KV head) the kernel touches reads its K and V once, up to the last key
+    any of its rows may see, plus the Q and O rows of its items and the request's block-table
+    entries, lengths and positions.  Flops: QK^T and PV over visible (row, key) pairs only."""
+    b = dev.b
+    e = b.elem_bytes
+    plan = pk.pensieve_debug_plan(dev.desc, 0)
+    keys, reqs = {}, set()
+    nbytes = flops = 0
+    pos_cache = {}
+    for kern, r, g, q0, qc, part, nparts, cost, h0, hc in plan:
+        if PLAN_KERNELS[int(kern)] != kernel or qc == 0:
+            continue
+        pos = pos_cache.setdefault(int(r), b.query_positions(int(r)))[q0:q0 + qc]
+        keys[(r, g)] = max(keys.get((r, g), 0), int(pos.max()) + 1)
+        reqs.add(int(r))
+        nbytes += 2 * int(qc) * int(hc) * b.head_dim * e
+        flops += 4 * b.head_dim * int(hc) * int((pos + 1).sum())
+    nbytes += sum(2 * k * b.head_dim * e for k in keys.values())
+    for r in reqs:
+        nbytes += 4 * (-(-int(b.context_lens[r]) // 16)) + 8 + (0 if b.has_default_positions else 4 * int(b.q_lens[r]))
+    return nbytes, flops
 
 
 def append_bytes(b) -> int:
@@ -187,11 +201,8 @@ def summarize_trace(trace, steps: int):
 
 
 def roofline_for(b, dev, per, kernel: str, counters):
-    reqs = kernel_requests(dev)
-    if kernel in ("attn_vector", "attn_mfma"):
-        rs = sorted(reqs[kernel])
-        nbytes = sum(request_bytes(b, r) for r in rs)
-        flops = sum(request_flops(b, r) for r in rs)
+    if kernel in PLAN_KERNELS.values():
+        nbytes, flops = kernel_work(dev, kernel)
     elif kernel == "kv_append":
         nbytes, flops = append_bytes(b), 0
     else:

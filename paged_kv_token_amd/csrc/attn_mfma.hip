@@ -22,6 +22,7 @@
 // consecutive keys, which is exactly the layout of the P^T operand, and the
 // V^T operand is one 16-byte LDS read of 8 consecutive keys of one dim row
 // (the V pool stores each block as [D][16], so V^T needs no transpose).
+#include <climits>
 #include <type_traits>
 
 #include "device_common.h"
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       qreg[ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(qp + (ks * 16 + 8 * h2) * 2));
   }
   const int pmax_w = uniform(wave_max_i(pos));
-  const int pmin_w = uniform(wave_min_i(pos));
+  const int pmin_w = uniform(wave_min_i(row_valid ? pos : INT_MAX));   // over valid rows only
   if (lane == 0) s_wmax[w] = pmax_w;
   __syncthreads();
   const int pmax_wg = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
@@ -224,9 +225,21 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     const int d = j * 32 + lane / 2;
     voff[j] = (uint32_t)(d * 32 + ((lane & 1) ^ vswz(d)) * 16);
   }
+  // Physical blocks this wave loads for tiles 0..127, held one per lane (lane l: tiles l and
+  // 64 + l) and read with v_readlane, so that no scalar-load latency sits on the per-tile
+  // path; later tiles of very long partitions read the block table with scalar loads.
+  // Past the partition any block of it serves (those keys are masked).
+  int btw0 = 0, btw1 = 0;
+  if (kb0 < kb1) {
+    const int lb0 = kb0 + 4 * lane + w, lb1 = kb0 + 4 * (64 + lane) + w;
+    btw0 = a.block_tables[(size_t)r * a.bt_stride + (lb0 < kb1 ? lb0 : kb0)];
+    btw1 = a.block_tables[(size_t)r * a.bt_stride + (lb1 < kb1 ? lb1 : kb0)];
+  }
   auto block_of = [&](int tile) {            // physical block loaded by this wave for `tile`
+    if (tile < 64) return __builtin_amdgcn_readlane(btw0, tile);
+    if (tile < 128) return __builtin_amdgcn_readlane(btw1, tile - 64);
     int lb = kb0 + 4 * tile + w;
-    lb = (lb < kb1) ? lb : kb0;              // past the partition: any block of it (masked)
+    lb = (lb < kb1) ? lb : kb0;
     return bt[lb];
   };
   auto issue = [&](const uint8_t* pool, const uint32_t* offs, int tile, uint8_t* stage) {
@@ -384,9 +397,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     }
   };
 
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   for (int ti = 0; ti < ntiles; ti += 2) {
-    tile_step(ti, std::integral_constant<int, 0>{}, s_cur, s_nxt);
-    if (ti + 1 < ntiles) tile_step(ti + 1, std::integral_constant<int, 1>{}, s_nxt, s_cur);
+    tile_step(ti, P0{}, s_cur, s_nxt);
+    if (ti + 1 < ntiles) tile_step(ti + 1, P1{}, s_nxt, s_cur);
   }
 
   // ---- epilogue: normalise, stage rows in LDS, store coalesced -----------------------------------
