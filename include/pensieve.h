@@ -122,9 +122,11 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
 /*
  * Workspace needed by pensieve_attn_fwd (num_partitions == 0) or by
  * pensieve_attn_split_partial (num_partitions >= 1) for this batch.  The
- * workspace holds the device copy of the work list; it is plain device
- * memory owned by the caller, needs no initialisation and may be reused by
- * the next call on the same stream.
+ * workspace holds the device copy of the work list and, when
+ * pensieve_attn_fwd splits long requests, their fp32 partial results
+ * (about rows x Hq x P x (head_dim + 2) x 4 bytes for the split requests'
+ * rows only); it is plain device memory owned by the caller, needs no
+ * initialisation and may be reused by the next call on the same stream.
  */
 pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, int32_t num_partitions,
                                              size_t* bytes);
@@ -137,6 +139,11 @@ pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, in
  *          request r (0-based) then sits at context_lens[r] - q_r + j.
  * o must not alias q.  Run the pensieve_kv_append of this step's rows first,
  * on the same stream.
+ * A request whose work items would run much longer than the batch's fair
+ * share (total KV blocks over all items / 1024, at least 64 blocks) is cut
+ * into P partitions of its blocks (split-KV, as in the PersistentKV paper,
+ * section 2); its partials go to the workspace and a final merge kernel
+ * combines them into o.  Short batches are never split.
  */
 pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* block_tables,

@@ -49,6 +49,12 @@ constexpr int kBlockSize = 16;
 constexpr int kVectorRowsMax = 8;    // query vectors per vector-kernel item
 constexpr int kMfmaRows = 128;       // query vectors per matrix-core item
 constexpr int kMaxPartitions = 256;
+// Adaptive split-KV of pensieve_attn_fwd: the plan aims at about kSplitTargetItems work
+// items of similar length (four workgroups per CU of MI355X's 256); a request whose one
+// item would be longer than that share is cut into partitions of at least kSplitMinBlocks
+// blocks (and at least one 64-key tile).
+constexpr long long kSplitTargetItems = 1024;
+constexpr long long kSplitMinBlocks = 64;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -115,11 +121,27 @@ struct Segment {
   int count;
 };
 
+// Workspace of a plan: [work items | per-request partial base rows | partial row map |
+// part_m | part_l | part_o], each 256-byte aligned; the last five exist only when
+// pensieve_attn_fwd splits some requests (compact partials: split requests' rows only).
 struct Plan {
   std::vector<pk::WorkItem> items;
   std::vector<PlannedItem> planned;   // same order as items
   std::vector<Segment> segments;
-  size_t bytes() const { return align_up(items.size() * sizeof(pk::WorkItem)); }
+  std::vector<int32_t> part_row_base;   // per request: first partial row, -1 if not split
+  std::vector<int32_t> rowmap;          // per partial row: {output row, partitions}
+  int split_rows = 0, pmax = 1, num_heads = 0, head_dim = 0;
+  size_t items_bytes() const { return align_up(items.size() * sizeof(pk::WorkItem)); }
+  size_t base_off() const { return items_bytes(); }
+  size_t rowmap_off() const { return base_off() + align_up(part_row_base.size() * sizeof(int32_t)); }
+  size_t meta_bytes() const { return rowmap_off() + align_up(rowmap.size() * sizeof(int32_t)); }
+  size_t partials() const { return (size_t)split_rows * num_heads * pmax; }
+  size_t pm_off() const { return meta_bytes(); }
+  size_t pl_off() const { return pm_off() + align_up(partials() * sizeof(float)); }
+  size_t po_off() const { return pl_off() + align_up(partials() * sizeof(float)); }
+  size_t bytes() const {
+    return split_rows ? po_off() + align_up(partials() * head_dim * sizeof(float)) : items_bytes();
+  }
 };
 
 bool matrix_ok(const pensieve_batch_desc* d) {
@@ -176,15 +198,72 @@ std::vector<PlannedItem> xcd_order(std::vector<PlannedItem> items) {
   return out;
 }
 
+// Work items of one request for one KV head and partition (no split): matrix-core items of
+// kMfmaRows query vectors, or vector items of at most kVectorRowsMax.
+long long items_per_kv_head(int q, int G, bool use_matrix) {
+  if (use_matrix) return (q + kMfmaRows / G - 1) / (kMfmaRows / G);
+  const int heads_per = std::min(G, kVectorRowsMax);
+  const int tok_per = std::max(1, kVectorRowsMax / heads_per);
+  return (long long)((G + heads_per - 1) / heads_per) * ((q + tok_per - 1) / tok_per);
+}
+
+// Partitions per request.  num_partitions >= 1: that many for every request (the explicit
+// split-KV pair).  0 (pensieve_attn_fwd): adaptive; an item's length is taken as its
+// request's block count, the fair share is the total over all items divided by
+// kSplitTargetItems, and a request is cut only when its items are longer than the share.
+std::vector<int> choose_partitions(const pensieve_batch_desc* d, int num_partitions) {
+  std::vector<int> P(d->num_reqs, num_partitions >= 1 ? num_partitions : 1);
+  if (num_partitions >= 1) return P;
+  const int G = d->num_heads / d->num_kv_heads;
+  const bool mat = matrix_ok(d);
+  long long total = 0;
+  for (int r = 0; r < d->num_reqs; ++r) {
+    const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+    if (q == 0) continue;
+    const long long nblk = (d->context_lens_host[r] + kBlockSize - 1) / kBlockSize;
+    const bool use_matrix = mat && (long long)q * G > kVectorRowsMax;
+    total += items_per_kv_head(q, G, use_matrix) * d->num_kv_heads * (nblk + 1);
+  }
+  const long long share = std::max(kSplitMinBlocks, total / kSplitTargetItems);
+  for (int r = 0; r < d->num_reqs; ++r) {
+    const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+    const long long nblk = (d->context_lens_host[r] + kBlockSize - 1) / kBlockSize;
+    if (q == 0 || nblk + 1 <= share) continue;
+    const long long want = (nblk + 1 + share - 1) / share;
+    P[r] = (int)std::max(1LL, std::min({want, (long long)kMaxPartitions, nblk / 4}));
+  }
+  return P;
+}
+
 void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
   const int G = d->num_heads / d->num_kv_heads;
   const bool mat = matrix_ok(d);
-  const int P = num_partitions >= 1 ? num_partitions : 1;
+  const std::vector<int> parts = choose_partitions(d, num_partitions);
+  plan.part_row_base.clear();
+  plan.rowmap.clear();
+  plan.split_rows = 0;
+  plan.pmax = 1;
+  plan.num_heads = d->num_heads;
+  plan.head_dim = d->head_dim;
+  if (num_partitions == 0) {
+    for (int r = 0; r < d->num_reqs; ++r) {
+      if (parts[r] <= 1) continue;
+      if (plan.part_row_base.empty()) plan.part_row_base.assign(d->num_reqs, -1);
+      plan.part_row_base[r] = plan.split_rows;
+      for (int i = d->cu_q_lens_host[r]; i < d->cu_q_lens_host[r + 1]; ++i) {
+        plan.rowmap.push_back(i);
+        plan.rowmap.push_back(parts[r]);
+      }
+      plan.split_rows += d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+      plan.pmax = std::max(plan.pmax, parts[r]);
+    }
+  }
   std::vector<PlannedItem> all;
   for (int r = 0; r < d->num_reqs; ++r) {
     const int L = d->context_lens_host[r];
     const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
     if (q == 0) continue;
+    const int P = parts[r];
     const long long nblk = (L + kBlockSize - 1) / kBlockSize;
     const long long per = (nblk + P - 1) / P;
     const bool use_matrix = mat && (long long)q * G > kVectorRowsMax;
@@ -389,9 +468,26 @@ int device_cu_count() {
 
 pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::AttnArgs& args, void* workspace,
                          hipStream_t stream) {
-  hipError_t e = stage_to_device(workspace, plan.items.data(), plan.items.size() * sizeof(pk::WorkItem), stream);
+  uint8_t* const ws = static_cast<uint8_t*>(workspace);
+  hipError_t e;
+  if (plan.split_rows == 0) {
+    e = stage_to_device(ws, plan.items.data(), plan.items.size() * sizeof(pk::WorkItem), stream);
+  } else {
+    // Items, partial base rows and the partial row map go up in one copy; the partials of
+    // the split requests live in the rest of the workspace and are merged at the end.
+    std::vector<uint8_t> meta(plan.meta_bytes(), 0);
+    std::memcpy(meta.data(), plan.items.data(), plan.items.size() * sizeof(pk::WorkItem));
+    std::memcpy(meta.data() + plan.base_off(), plan.part_row_base.data(), plan.part_row_base.size() * sizeof(int32_t));
+    std::memcpy(meta.data() + plan.rowmap_off(), plan.rowmap.data(), plan.rowmap.size() * sizeof(int32_t));
+    e = stage_to_device(ws, meta.data(), meta.size(), stream);
+    args.part_row_base = reinterpret_cast<const int32_t*>(ws + plan.base_off());
+    args.part_m = reinterpret_cast<float*>(ws + plan.pm_off());
+    args.part_l = reinterpret_cast<float*>(ws + plan.pl_off());
+    args.part_o = reinterpret_cast<float*>(ws + plan.po_off());
+    args.part_stride = plan.pmax;
+  }
   if (e != hipSuccess) return hip_fail(e, "work-list upload");
-  const pk::WorkItem* dev_items = static_cast<const pk::WorkItem*>(workspace);
+  const pk::WorkItem* dev_items = reinterpret_cast<const pk::WorkItem*>(ws);
   bool has_matrix = false, has_vector = false;
   for (const Segment& s : plan.segments) (s.kernel == kMatrix ? has_matrix : has_vector) = true;
   Concurrency* conc = nullptr;
@@ -423,6 +519,13 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
   if (fork) {
     if ((e = hipEventRecord(conc->join, conc->side)) != hipSuccess) return hip_fail(e, "join event");
     if ((e = hipStreamWaitEvent(stream, conc->join, 0)) != hipSuccess) return hip_fail(e, "join wait");
+  }
+  if (plan.split_rows > 0) {
+    const int rows = plan.split_rows * d->num_heads;
+    TraceScope trace(kTraceMerge, rows, stream);
+    e = pk::launch_split_merge(args.part_o, args.part_m, args.part_l, rows, d->num_heads, d->head_dim, plan.pmax,
+                               reinterpret_cast<const int32_t*>(ws + plan.rowmap_off()), d->dtype, args.o, stream);
+    if (e != hipSuccess) return hip_fail(e, "split merge launch");
   }
   return ok();
 }
@@ -557,8 +660,8 @@ pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part
   if (rows > (1LL << 31) - 4) return fail(PENSIEVE_ERR_UNSUPPORTED, "too many rows");
   if (!part_o || !part_m || !part_l || !o) return fail(PENSIEVE_ERR_INVALID_ARG, "a pointer is NULL");
   TraceScope trace(kTraceMerge, (int)rows, static_cast<hipStream_t>(stream));
-  hipError_t e = pk::launch_split_merge(part_o, part_m, part_l, (int)rows, head_dim, num_partitions, dtype, o,
-                                        static_cast<hipStream_t>(stream));
+  hipError_t e = pk::launch_split_merge(part_o, part_m, part_l, (int)rows, num_heads, head_dim, num_partitions, nullptr,
+                                        dtype, o, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "split merge launch");
   return ok();
 }

@@ -421,9 +421,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       }
   }
   const bool split = a.write_partials || it.num_parts > 1;
+  // Partial row of the item's first query row (partials of split requests may be compacted).
+  const size_t prow0 = (a.part_row_base ? (size_t)a.part_row_base[r] : (size_t)row0) + it.q_begin;
   if (split && h2 == 0 && row_valid) {
     // Report l relative to the true max: l_top = l_tot * exp2((m_run - m_top) c).
-    const size_t pi = (qrow * Hq + h) * a.part_stride + it.part;
+    const size_t pi = ((prow0 + tok) * Hq + h) * a.part_stride + it.part;
     const bool any = m_top != -INFINITY;
     a.part_m[pi] = any ? m_top * a.scale : -INFINITY;
     a.part_l[pi] = any ? l_tot * fast_exp2((m_run - m_top) * c) : 0.f;
@@ -455,8 +457,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       const int otok = rr / G;
       if (otok >= it.q_count) continue;
       const f32x4 val = *reinterpret_cast<const f32x4*>(lds + rr * OROW + cc * 16);
-      const size_t orow_g = (size_t)row0 + it.q_begin + otok;
-      const size_t pi = (orow_g * Hq + g * G + (rr % G)) * a.part_stride + it.part;
+      const size_t pi = ((prow0 + otok) * Hq + g * G + (rr % G)) * a.part_stride + it.part;
       *reinterpret_cast<f32x4*>(a.part_o + pi * D + cc * 4) = val;
     }
   }

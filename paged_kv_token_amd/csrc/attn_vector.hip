@@ -200,6 +200,8 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   __syncthreads();
 
   const bool split = a.write_partials || it.num_parts > 1;
+  // Partial row of the item's first query row (partials of split requests may be compacted).
+  const size_t prow0 = (a.part_row_base ? (size_t)a.part_row_base[r] : (size_t)row0) + it.q_begin;
   for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
     const int n = idx / D, d = idx % D;
     float M = s_m[0][n];
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
     if (!split) {
       store_elem<DT>(a.o, (row * Hq + h) * D + d, o);
     } else {
-      const size_t pi = (row * Hq + h) * a.part_stride + it.part;
+      const size_t pi = ((prow0 + tok) * Hq + h) * a.part_stride + it.part;
       a.part_o[pi * D + d] = o;
       if (d == 0) {
         a.part_m[pi] = (M == -INFINITY) ? -INFINITY : M * a.scale;

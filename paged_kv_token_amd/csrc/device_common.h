@@ -39,9 +39,10 @@ struct AttnArgs {
   const int32_t* cu_q_lens;
   const int32_t* q_pos;      // may be null
   uint8_t* o;
-  float* part_o;             // [T][Hq][P][D] when items are split
-  float* part_m;             // [T][Hq][P]
-  float* part_l;             // [T][Hq][P]
+  float* part_o;             // [rows][Hq][P][D] when items are split
+  float* part_m;             // [rows][Hq][P]
+  float* part_l;             // [rows][Hq][P]
+  const int32_t* part_row_base;   // per request: partial row of its first query row (null: the query row itself)
   const WorkItem* items;
   int32_t num_items;
   int32_t num_heads;
@@ -51,7 +52,6 @@ struct AttnArgs {
   int32_t write_partials;    // 1: every item writes (m, l, O_p); 0: items with num_parts == 1 write O
   float scale;               // softmax scale on q.k
   float scale_log2;          // scale * log2(e)
-  int32_t pad_;
 };
 
 // ---- element conversion ----------------------------------------------------

@@ -21,8 +21,10 @@ hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int head_dim, int
 // whole head group), fp16/bf16 only.
 hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int head_dim, int group, hipStream_t stream);
 
-// Merge of split partials into O.
-hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows,
-                              int head_dim, int num_partitions, int dtype, void* o, hipStream_t stream);
+// Merge of split partials into O: rows = partial rows x num_heads; rowmap
+// (nullable) gives each partial row's output row and partition count.
+hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows, int num_heads,
+                              int head_dim, int num_partitions, const int32_t* rowmap, int dtype, void* o,
+                              hipStream_t stream);
 
 }  // namespace pk

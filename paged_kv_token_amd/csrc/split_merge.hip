@@ -9,6 +9,12 @@
 // One wave per (row, head): lanes read the P (m, l) pairs, reduce the max and
 // the weight sum across the wave, park the weights in LDS, then stream the P
 // partial rows of D fp32 values with coalesced loads (lane = dim).
+//
+// Partials are laid out [row][head][P_stride]; with a row map, partial row c
+// holds output row rowmap[2c] and only its first rowmap[2c + 1] partitions
+// (the split-KV of pensieve_attn_fwd keeps only split requests' rows, each
+// with its own partition count); without one, partial row c is output row c
+// with P_stride partitions.
 #include "device_common.h"
 #include "launch.h"
 
@@ -19,14 +25,22 @@ constexpr int kMaxMergePartitions = 256;
 template <int DT, int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_m,
-                                                          const float* __restrict__ part_l, int rows, int P,
+                                                          const float* __restrict__ part_l, int rows, int num_heads,
+                                                          int P_stride, const int32_t* __restrict__ rowmap,
                                                           uint8_t* __restrict__ o) {
   __shared__ float s_w[4][kMaxMergePartitions];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int rh = blockIdx.x * 4 + wv;
   if (rh >= rows) return;  // whole wave leaves together; no block barrier follows
-  const size_t base = (size_t)rh * P;
+  const size_t base = (size_t)rh * P_stride;
+  size_t out = rh;         // output (row, head) index
+  int P = P_stride;
+  if (rowmap) {
+    const int c = rh / num_heads;
+    out = (size_t)rowmap[2 * c] * num_heads + rh % num_heads;
+    P = rowmap[2 * c + 1];
+  }
   constexpr float kLog2e = 1.4426950408889634f;
 
   float M = -INFINITY;
@@ -54,28 +68,35 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
       const float wgt = s_w[wv][p];
       if (wgt != 0.f) acc = fmaf(wgt, part_o[(base + p) * D + d], acc);
     }
-    store_elem<DT>(o, (size_t)rh * D + d, acc * inv);
+    store_elem<DT>(o, out * D + d, acc * inv);
   }
 }
 
 template <int DT>
-static hipError_t launch_merge_dt(const float* po, const float* pm, const float* pl, int rows, int head_dim, int P,
-                                  void* o, hipStream_t stream) {
+static hipError_t launch_merge_dt(const float* po, const float* pm, const float* pl, int rows, int num_heads,
+                                  int head_dim, int P, const int32_t* rowmap, void* o, hipStream_t stream) {
   dim3 grid((rows + 3) / 4), block(256);
   if (head_dim == 64)
-    hipLaunchKernelGGL((split_merge_kernel<DT, 64>), grid, block, 0, stream, po, pm, pl, rows, P, (uint8_t*)o);
+    hipLaunchKernelGGL((split_merge_kernel<DT, 64>), grid, block, 0, stream, po, pm, pl, rows, num_heads, P, rowmap,
+                       (uint8_t*)o);
   else
-    hipLaunchKernelGGL((split_merge_kernel<DT, 128>), grid, block, 0, stream, po, pm, pl, rows, P, (uint8_t*)o);
+    hipLaunchKernelGGL((split_merge_kernel<DT, 128>), grid, block, 0, stream, po, pm, pl, rows, num_heads, P, rowmap,
+                       (uint8_t*)o);
   return hipGetLastError();
 }
 
-hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows,
-                              int head_dim, int num_partitions, int dtype, void* o, hipStream_t stream) {
+hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows, int num_heads,
+                              int head_dim, int num_partitions, const int32_t* rowmap, int dtype, void* o,
+                              hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   switch (dtype) {
-    case kF32: return launch_merge_dt<kF32>(part_o, part_m, part_l, rows, head_dim, num_partitions, o, stream);
-    case kF16: return launch_merge_dt<kF16>(part_o, part_m, part_l, rows, head_dim, num_partitions, o, stream);
-    default: return launch_merge_dt<kBF16>(part_o, part_m, part_l, rows, head_dim, num_partitions, o, stream);
+    case kF32:
+      return launch_merge_dt<kF32>(part_o, part_m, part_l, rows, num_heads, head_dim, num_partitions, rowmap, o, stream);
+    case kF16:
+      return launch_merge_dt<kF16>(part_o, part_m, part_l, rows, num_heads, head_dim, num_partitions, rowmap, o, stream);
+    default:
+      return launch_merge_dt<kBF16>(part_o, part_m, part_l, rows, num_heads, head_dim, num_partitions, rowmap, o,
+                                    stream);
   }
 }
 

@@ -108,6 +108,7 @@ def run_attn(gb: GpuBatch, flags: int = 0):
     import torch
     desc = gb.make_desc(flags)
     ws = torch.empty(max(pk.pensieve_attn_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)    # every float in it reads as NaN until the library writes it
     o = torch.empty_like(gb.q)
     poison_(o, gb.batch.dtype)
     pk.pensieve_attn_fwd(desc, gb.q, gb.k_pool, gb.v_pool, gb.block_tables, gb.context_lens, gb.cu_q_lens,

@@ -80,24 +80,37 @@ def test_null_pointers_rejected_without_gpu(lib):
     assert lib.pensieve_attn_workspace_size(None, 0, None) == 1
 
 
-def _coverage(b, plan, P=1):
-    """Every (row, query head, partition) appears exactly once."""
-    seen = np.zeros((b.total_q, b.num_heads, P), dtype=np.int32)
+def _coverage(b, plan, P=None):
+    """Every (row, query head) is covered once in each of its request's partitions 0..P_r-1
+    (P_r fixed to P when given, else the request's own count, the same on all its items)."""
+    parts = {}
+    for row in plan[plan[:, 4] > 0]:
+        parts.setdefault(int(row[1]), set()).add(int(row[6]))
+    Pmax = max([P or 1] + [max(v) for v in parts.values()])
+    seen = np.zeros((b.total_q, b.num_heads, Pmax), dtype=np.int32)
+    want = np.zeros_like(seen)
     G = b.num_heads // b.num_kv_heads
+    for r in range(b.num_reqs):
+        counts = parts.get(r, {P or 1})
+        assert len(counts) == 1, f"request {r} has items with different partition counts"
+        pr = counts.pop()
+        assert P is None or pr == P
+        want[int(b.cu_q_lens[r]):int(b.cu_q_lens[r + 1]), :, :pr] = 1
     for kern, r, g, q0, qc, part, nparts, cost, h0, hc in plan:
-        assert nparts == P and 0 <= part < P
+        assert 0 <= part < nparts and (P is None or nparts == P)
         lo = int(b.cu_q_lens[r]) + q0
         assert q0 + qc <= int(b.q_lens[r])
         for h in range(g * G + h0, g * G + h0 + hc):
             seen[lo:lo + qc, h, part] += 1
-    return seen
+    return seen, want
 
 
 @pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
 def test_plan_covers_each_row_head_once(lib, index):
     b = config_batch(index)
     plan = pk.pensieve_debug_plan(desc_for(b))
-    assert np.all(_coverage(b, plan) == 1)
+    seen, want = _coverage(b, plan)
+    assert np.array_equal(seen, want)
     mat = plan[plan[:, 0] == 1]
     if len(mat) >= 16:
         # matrix-core items: interleaved over 8 XCD bins (slot % 8); each bin runs longest first and
@@ -117,7 +130,50 @@ def test_plan_covers_each_row_head_once(lib, index):
 def test_split_plan_covers_each_partition(lib, P):
     b = config_batch(4, num_heads=4, max_hist=3000)
     plan = pk.pensieve_debug_plan(desc_for(b), P)
-    assert np.all(_coverage(b, plan, P) == 1)
+    seen, want = _coverage(b, plan, P)
+    assert np.array_equal(seen, want) and want.all()
+
+
+def _adaptive_parts(b):
+    plan = pk.pensieve_debug_plan(desc_for(b))
+    out = {}
+    for row in plan[plan[:, 4] > 0]:
+        out[int(row[1])] = int(row[6])
+    return out
+
+
+@pytest.mark.parametrize("index", [0, 1, 2, 3])
+def test_adaptive_split_leaves_ordinary_batches_whole(lib, index):
+    assert set(_adaptive_parts(config_batch(index)).values()) == {1}
+
+
+def test_adaptive_split_cuts_only_the_long_requests(lib):
+    """Long-context batch: the longest histories get the most partitions, at least 64
+    blocks each; a batch of short requests beside one long one splits only the long one."""
+    b = config_batch(4)
+    parts = _adaptive_parts(b)
+    nblk = -(-b.context_lens // 16)
+    assert all(parts[r] > 1 for r in range(b.num_reqs))
+    order = np.argsort(nblk, kind="stable")
+    assert [parts[int(r)] for r in order] == sorted(parts[int(r)] for r in order)
+    assert all(nblk[r] / parts[r] >= 4 for r in parts)
+    mixed = custom_batch([20000] + [300] * 12, [1] * 13, num_heads=8, num_kv_heads=8, head_dim=128, dtype="f16",
+                         seed=9)
+    mp = _adaptive_parts(mixed)
+    assert mp[0] > 1 and all(mp[r] == 1 for r in range(1, 13))
+
+
+def test_adaptive_split_workspace_holds_the_partials(lib):
+    b = config_batch(4)
+    d = desc_for(b)
+    parts = _adaptive_parts(b)
+    n_items = len(pk.pensieve_debug_plan(d))
+    rows = sum(int(b.q_lens[r]) for r, p in parts.items() if p > 1)
+    partials = rows * b.num_heads * max(parts.values())
+    ws = pk.pensieve_attn_workspace_size(d)
+    assert ws % 256 == 0
+    assert ws >= 32 * n_items + partials * (b.head_dim + 2) * 4
+    assert ws < 32 * n_items + partials * (b.head_dim + 2) * 4 + 6 * 256 + 4 * (b.num_reqs + 2 * rows)
 
 
 def test_routing_rules(lib):

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import paged_kv_token_amd as pk
-from gpu_harness import run_split, to_f64, upload
+from gpu_harness import run_attn, run_split, to_f64, upload
 from oracle_helpers import oracle_output, oracle_pools, oracle_split
 from workloads import config_batch, custom_batch
 
@@ -51,3 +51,36 @@ def test_split_partials_and_merge(name, path):
     err = float(np.max(np.abs(o - ref)))
     _say(f"{name}/{path}: merged max abs err {err:.3e}")
     assert err <= tol
+
+
+ADAPTIVE = {
+    # one long decode request among short ones: only it is cut (vector kernel partials)
+    "long_decode_among_short_f16": lambda: custom_batch([20000] + [300] * 12, [1] * 13, num_heads=8, num_kv_heads=8,
+                                                        head_dim=128, dtype="f16", seed=61),
+    # long prefill (matrix-core partials, GQA) and long decode beside a short request
+    "long_prefill_gqa_bf16": lambda: custom_batch([6000, 9000, 200], [300, 1, 5], num_heads=8, num_kv_heads=2,
+                                                  head_dim=128, dtype="bf16", seed=62),
+    # partially evicted history recomputed ahead of new rows, d = 64
+    "recompute_d64_f16": lambda: custom_batch([5000, 40], [64, 3], [1504, 0], num_heads=4, num_kv_heads=4,
+                                              head_dim=64, dtype="f16", seed=63),
+}
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("name", sorted(ADAPTIVE))
+def test_adaptive_split_in_attn_fwd(name, path):
+    """pensieve_attn_fwd cuts the long requests (checked on the plan) and still matches the oracle;
+    the workspace starts as NaN, so a partial the merge reads without a kernel writing it shows."""
+    b = ADAPTIVE[name]()
+    gb = upload(b)
+    plan = pk.pensieve_debug_plan(gb.make_desc(PATHS[path]))
+    parts = {int(row[1]): int(row[6]) for row in plan[plan[:, 4] > 0]}
+    longest = int(np.argmax(b.context_lens))
+    _say(f"adaptive {name}/{path}: partitions {parts}")
+    assert parts[longest] > 1 and min(parts.values()) == 1
+    ref = oracle_output(b)
+    got = to_f64(run_attn(gb, PATHS[path]))
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - ref)))
+    _say(f"adaptive {name}/{path}: max abs err {err:.3e}")
+    assert err <= 1e-2
