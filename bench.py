@@ -156,7 +156,12 @@ def kernel_work(dev: DeviceBatch, kernel: str):
         keys[(r, g)] = max(keys.get((r, g), 0), int(pos.max()) + 1)
         reqs.add(int(r))
         nbytes += 2 * int(qc) * int(hc) * b.head_dim * e
-        flops += 4 * b.head_dim * int(hc) * int((pos + 1).sum())
+        # keys of the item's partition (its share of the request's blocks) each row may see
+        L = int(b.context_lens[r])
+        per = -(-(-(-L // 16)) // int(nparts)) * 16
+        k0, k1 = int(part) * per, min((int(part) + 1) * per, L)
+        seen = np.clip(np.minimum(pos + 1, k1) - k0, 0, None)
+        flops += 4 * b.head_dim * int(hc) * int(seen.sum())
     nbytes += sum(2 * k * b.head_dim * e for k in keys.values())
     for r in reqs:
         nbytes += 4 * (-(-int(b.context_lens[r]) // 16)) + 8 + (0 if b.has_default_positions else 4 * int(b.q_lens[r]))
