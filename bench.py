@@ -7,7 +7,9 @@ pools (kv_append), and run the attention of every query row over its
 request's paged KV (attn_fwd).  The workload is the Llama-2-13B-shaped mixed
 batch (40 heads, head_dim 128, fp16; 32 conversations with 16-128 new tokens
 plus 32 decode requests, histories of 256-2048 tokens), generated from a
-fixed seed and resident in HBM before the timed region starts.
+fixed seed and resident in HBM before the timed region starts.  Consecutive
+steps alternate between two copies of the batch, so no step reads K/V or Q
+left in the last-level cache by the step before.
 
 Prints ONE JSON line with the headline metric (query tokens/s), a roofline
 object for the dominant kernel (per-launch durations come from HIP events the
@@ -60,9 +62,13 @@ def source_digest(kernel: str) -> str:
 # device-side batch
 # ---------------------------------------------------------------------------
 class DeviceBatch:
-    """A seeded batch resident in HBM: pools filled with its cached history."""
+    """A seeded batch resident in HBM: pools filled with its cached history.
 
-    def __init__(self, batch):
+    `copies` independent copies of the pools, Q and O are kept and consecutive steps rotate
+    through them, so a step's K/V and Q cannot still sit in the 256 MB last-level cache
+    (MALL) from the step before (the working set of two copies exceeds it on every workload)."""
+
+    def __init__(self, batch, copies: int = 2):
         import torch
         self.b = b = batch
         td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[b.dtype]
@@ -89,7 +95,16 @@ class DeviceBatch:
                                  dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
                                  context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens)
         self.ws = torch.empty(max(pk.pensieve_attn_workspace_size(self.desc), 256), dtype=torch.uint8, device="cuda")
+        self.sets = [(self.k_pool, self.v_pool, self.q, self.o)]
+        for _ in range(copies - 1):
+            self.sets.append((self.k_pool.clone(), self.v_pool.clone(), self.q.clone(), torch.empty_like(self.o)))
+        self.turn = 0
         torch.cuda.synchronize()
+
+    def _next(self):
+        s = self.sets[self.turn % len(self.sets)]
+        self.turn += 1
+        return s
 
     def _dev(self, arr):
         import torch
@@ -98,15 +113,21 @@ class DeviceBatch:
         return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
     def step(self):
-        pk.pensieve_kv_append(self.k_new, self.v_new, self.k_pool, self.v_pool, self.new_slots)
-        pk.pensieve_attn_fwd(self.desc, self.q, self.k_pool, self.v_pool, self.bt, self.ctx, self.cu, self.q_pos,
-                             self.o, self.ws)
+        """The whole path: append the step's new rows, then attention over the batch."""
+        k_pool, v_pool, q, o = self._next()
+        pk.pensieve_kv_append(self.k_new, self.v_new, k_pool, v_pool, self.new_slots)
+        pk.pensieve_attn_fwd(self.desc, q, k_pool, v_pool, self.bt, self.ctx, self.cu, self.q_pos, o, self.ws)
+
+    def attn(self):
+        k_pool, v_pool, q, o = self._next()
+        pk.pensieve_attn_fwd(self.desc, q, k_pool, v_pool, self.bt, self.ctx, self.cu, self.q_pos, o, self.ws)
 
     def split_step(self, P, bufs):
         po, pm, pl, ws = bufs
-        pk.pensieve_attn_split_partial(self.desc, P, self.q, self.k_pool, self.v_pool, self.bt, self.ctx, self.cu,
-                                       self.q_pos, po, pm, pl, ws)
-        pk.pensieve_attn_split_merge(po, pm, pl, self.o)
+        k_pool, v_pool, q, o = self._next()
+        pk.pensieve_attn_split_partial(self.desc, P, q, k_pool, v_pool, self.bt, self.ctx, self.cu, self.q_pos,
+                                       po, pm, pl, ws)
+        pk.pensieve_attn_split_merge(po, pm, pl, o)
 
     def split_buffers(self, P):
         import torch
@@ -240,6 +261,38 @@ def load_counters():
 
 
 # ---------------------------------------------------------------------------
+def copy_bandwidth(mib: int = 1024, reps: int = 10):
+    """Achievable HBM bandwidth on this GPU: a device-to-device copy of `mib` MiB (read + write)."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbs": round(gbs, 1), "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4),
+            "what": f"{mib} MiB device-to-device copy, bytes read + written"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(b, budget_s: float):
     """The CPU oracle (as it stands) on this host: all requests, as many query heads as fit the budget."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -265,7 +318,7 @@ def cpu_baseline(b, budget_s: float):
     rate = b.total_q * (done / b.num_heads) / elapsed
     return {"value": round(rate, 2), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"all {b.num_reqs} requests x query heads 0..{done - 1} of {b.num_heads} "
-                      f"({elapsed:.1f} s, float64 NumPy; rate scaled to all heads)"}
+                      f"({elapsed:.1f} s, float64 NumPy on {cpu_model()}; rate scaled to all heads)"}
 
 
 def secondary(index: int, steps: int, warmup: int, counters):
@@ -274,8 +327,7 @@ def secondary(index: int, steps: int, warmup: int, counters):
     b = config_batch(index)
     dev = DeviceBatch(b)
     out = {"workload": b.name, "total_q": b.total_q}
-    ms, trace = time_steps(lambda: pk.pensieve_attn_fwd(dev.desc, dev.q, dev.k_pool, dev.v_pool, dev.bt, dev.ctx,
-                                                        dev.cu, dev.q_pos, dev.o, dev.ws), steps, warmup)
+    ms, trace = time_steps(dev.attn, steps, warmup)
     per = summarize_trace(trace, steps)
     attn = {k: v for k, v in per.items() if k.startswith("attn")}
     dom = max(attn, key=lambda k: attn[k]["total_ms"])
@@ -357,6 +409,7 @@ def main():
                             "hbm_frac": round(total_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del dev
     torch.cuda.empty_cache()
+    result["hbm_copy"] = copy_bandwidth()
     if not args.no_secondary:
         result["secondary"] = []
         for idx in (2, 3, 4):
