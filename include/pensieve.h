@@ -194,13 +194,19 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
 
 /*
  * Per-launch timing trace.  While enabled, every kernel the library
- * launches is bracketed by a pair of hipEvents recorded on the launch
- * stream.  pensieve_trace_read waits for the recorded launches to finish,
- * writes up to max_records records {kernel, work items, milliseconds}
- * (kernel: 0 kv_append, 1 vector attention, 2 matrix-core attention,
- * 3 split merge), sets *num_records to the number written, and clears the
- * trace.  The events come from a pool created on first enable (per device)
- * and reused.  Tracing is off by default and costs nothing when off.
+ * launches records start and stop events through its own dispatch packet
+ * (hipExtLaunchKernel), so tracing adds no packets to the stream.
+ * pensieve_trace_read waits for the traced launches still in flight,
+ * writes up to max_records records {kernel, work items, milliseconds} in
+ * launch order (kernel: 0 kv_append, 1 vector attention, 2 matrix-core
+ * attention, 3 split merge), sets *num_records to the number written, and
+ * clears the trace (at most 65536 records are kept between reads).
+ * enable > 0 turns tracing on and times every enable-th launch of each kernel
+ * kind (1: every launch); 0 turns it off.  A timed launch costs more than an
+ * ordinary one (about 15 us of host time with ROCm 7.2, more the first time
+ * an event is used), so a loop should warm up traced before it is measured.
+ * Enabling fills a pool of reusable events (a few hundred, on the current
+ * device).  Tracing is off by default and costs nothing when off.
  */
 typedef struct pensieve_trace_record {
   int32_t kernel;

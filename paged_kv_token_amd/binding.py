@@ -210,8 +210,9 @@ def pensieve_debug_plan(desc: BatchDesc, num_partitions: int = 0) -> np.ndarray:
     return out[:n.value]
 
 
-def pensieve_trace_enable(enable: bool = True) -> None:
-    _check(load_library().pensieve_trace_enable(1 if enable else 0))
+def pensieve_trace_enable(enable=True, every: int = 1) -> None:
+    """Turn launch timing on (every `every`-th launch of each kernel kind) or off."""
+    _check(load_library().pensieve_trace_enable(max(1, int(every)) if enable else 0))
 
 
 def pensieve_trace_read(max_records: int = 1 << 16):

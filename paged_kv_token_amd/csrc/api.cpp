@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -21,6 +22,13 @@
 
 #include "launch.h"
 #include "pensieve.h"
+
+namespace pk {
+LaunchEvents& launch_events() {
+  thread_local LaunchEvents ev;
+  return ev;
+}
+}  // namespace pk
 
 namespace {
 
@@ -152,50 +160,47 @@ bool matrix_ok(const pensieve_batch_desc* d) {
 
 // Workgroup i of a launch runs on XCD i % kXcds, and each XCD has its own L2.
 // Matrix-core items of one (request, KV head, partition) stream the same K/V,
-// so they are kept on one XCD: such groups are spread over kXcds bins by cost
-// (largest group first into the lightest bin), each bin lists its items longest
-// first, and the bins are interleaved so that bin x occupies launch slots
-// x, x + kXcds, ...  Bins are padded to equal length with zero-row items, which
-// the kernel leaves at once.
+// so they are kept on one XCD: such groups, longest first, go one by one to the
+// least loaded of kXcds bins; each bin then lists its items longest first, and
+// the bins are interleaved so that bin x occupies launch slots x, x + kXcds, ...
+// Bins are padded to equal length with zero-row items, which the kernel leaves
+// at once.
 constexpr int kXcds = 8;
 
-std::vector<PlannedItem> xcd_order(std::vector<PlannedItem> items) {
-  if (items.size() < 2 * kXcds) return items;
-  struct Group { long long cost = 0; std::vector<PlannedItem> items; };
-  std::vector<Group> groups;
-  std::unordered_map<long long, size_t> index;
-  for (const PlannedItem& p : items) {
-    const long long k = ((long long)p.w.req * 65536 + p.w.kv_head) * 1024 + p.w.part;
-    auto it = index.find(k);
-    if (it == index.end()) {
-      index[k] = groups.size();
-      groups.push_back({});
-      it = index.find(k);
-    }
-    groups[it->second].cost += p.cost;
-    groups[it->second].items.push_back(p);
+// One (request, KV head, partition) of matrix-core items: items[first, first + count), all of
+// the same cost.
+struct ItemGroup {
+  long long cost;
+  int first, count;
+};
+
+void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGroup>& groups,
+               std::vector<PlannedItem>& out) {
+  std::vector<int> order(groups.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return groups[a].cost > groups[b].cost; });
+  if (items.size() < 2 * kXcds) {
+    for (int gi : order)
+      out.insert(out.end(), items.begin() + groups[gi].first, items.begin() + groups[gi].first + groups[gi].count);
+    return;
   }
-  std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.cost > b.cost; });
-  std::vector<std::vector<PlannedItem>> bins(kXcds);
-  std::vector<long long> load(kXcds, 0);
-  for (Group& g : groups) {
-    const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-    load[x] += g.cost;
-    bins[x].insert(bins[x].end(), g.items.begin(), g.items.end());
+  std::vector<int> bins[kXcds];
+  long long load[kXcds] = {};
+  for (int gi : order) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    load[x] += groups[gi].cost * groups[gi].count;
+    for (int k = 0; k < groups[gi].count; ++k) bins[x].push_back(groups[gi].first + k);
   }
   size_t longest = 0;
-  for (auto& b : bins) {
-    std::stable_sort(b.begin(), b.end(), [](const PlannedItem& a, const PlannedItem& c) { return a.cost > c.cost; });
-    longest = std::max(longest, b.size());
-  }
-  std::vector<PlannedItem> out;
-  out.reserve(longest * kXcds);
+  for (auto& bin : bins) longest = std::max(longest, bin.size());
   PlannedItem filler = items.front();
   filler.w.q_count = 0;
   filler.cost = 0;
+  out.reserve(out.size() + longest * kXcds);
   for (size_t k = 0; k < longest; ++k)
-    for (int x = 0; x < kXcds; ++x) out.push_back(k < bins[x].size() ? bins[x][k] : filler);
-  return out;
+    for (int x = 0; x < kXcds; ++x) out.push_back(k < bins[x].size() ? items[bins[x][k]] : filler);
 }
 
 // Work items of one request for one KV head and partition (no split): matrix-core items of
@@ -258,11 +263,24 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
       plan.pmax = std::max(plan.pmax, parts[r]);
     }
   }
-  std::vector<PlannedItem> all;
-  for (int r = 0; r < d->num_reqs; ++r) {
+  // Requests longest first (by KV blocks), so that every list below comes out longest first
+  // without sorting its items.
+  // Scratch lists keep their capacity from call to call (one set per host thread).
+  thread_local std::vector<int> reqs;
+  thread_local std::vector<PlannedItem> mat_items;
+  thread_local std::vector<ItemGroup> groups;
+  thread_local std::vector<PlannedItem> vec[4];   // vector items by width 1, 2, 4, 8 query vectors
+  reqs.clear();
+  mat_items.clear();
+  groups.clear();
+  for (auto& v : vec) v.clear();
+  for (int r = 0; r < d->num_reqs; ++r)
+    if (d->cu_q_lens_host[r + 1] > d->cu_q_lens_host[r]) reqs.push_back(r);
+  std::stable_sort(reqs.begin(), reqs.end(),
+                   [&](int a, int b) { return d->context_lens_host[a] > d->context_lens_host[b]; });
+  for (int r : reqs) {
     const int L = d->context_lens_host[r];
     const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
-    if (q == 0) continue;
     const int P = parts[r];
     const long long nblk = (L + kBlockSize - 1) / kBlockSize;
     const long long per = (nblk + P - 1) / P;
@@ -272,13 +290,15 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
       for (int g = 0; g < d->num_kv_heads; ++g) {
         if (use_matrix) {
           const int tok_tile = kMfmaRows / G;
+          groups.push_back({(blocks + 1) * 64, (int)mat_items.size(), 0});
           for (int q0 = 0; q0 < q; q0 += tok_tile) {
             PlannedItem p{};
             p.w = {r, q0, std::min(tok_tile, q - q0), g, 0, G, part, P};
             p.kernel = kMatrix;
             p.param = G;
             p.cost = (blocks + 1) * 64;
-            all.push_back(p);
+            mat_items.push_back(p);
+            groups.back().count++;
           }
         } else {
           const int heads_per = std::min(G, kVectorRowsMax);
@@ -292,26 +312,21 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
               p.kernel = kVector;
               p.param = next_pow2(qc * hc);
               p.cost = (blocks + 1) * (4 + qc * hc);
-              all.push_back(p);
+              vec[p.param == 1 ? 0 : p.param == 2 ? 1 : p.param == 4 ? 2 : 3].push_back(p);
             }
           }
         }
       }
     }
   }
-  // Segments: matrix items first, then vector items by width; longest first inside each.
-  auto key = [](const PlannedItem& p) { return p.kernel == kMatrix ? 0 : p.param; };
-  std::stable_sort(all.begin(), all.end(), [&](const PlannedItem& a, const PlannedItem& b) {
-    if (key(a) != key(b)) return key(a) < key(b);
-    return a.cost > b.cost;
-  });
-  size_t nmat = 0;
-  while (nmat < all.size() && all[nmat].kernel == kMatrix) ++nmat;
-  std::vector<PlannedItem> ordered = xcd_order(std::vector<PlannedItem>(all.begin(), all.begin() + nmat));
-  ordered.insert(ordered.end(), all.begin() + nmat, all.end());
+  // Launch order: the matrix-core segment (spread over the XCDs), then vector items by width.
+  std::vector<PlannedItem>& ordered = plan.planned;
+  ordered.clear();
+  if (!mat_items.empty()) xcd_order(mat_items, groups, ordered);
+  for (auto& v : vec) ordered.insert(ordered.end(), v.begin(), v.end());
   plan.items.clear();
+  plan.items.reserve(ordered.size());
   plan.segments.clear();
-  plan.planned = ordered;
   for (size_t i = 0; i < ordered.size(); ++i) {
     plan.items.push_back(ordered[i].w);
     if (plan.segments.empty() || plan.segments.back().kernel != ordered[i].kernel ||
@@ -323,13 +338,15 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
 }
 
 // ---- pinned staging of work lists ---------------------------------------------------------
-// Each device gets a small ring of page-locked host buffers; a work list is
-// copied into the next one and sent with hipMemcpyAsync on the caller's
-// stream.  An event per buffer guards its reuse until the copy has finished.
+// Each device gets a small ring of page-locked, device-mapped host buffers; a
+// work list is copied into the next one and pulled into the workspace by a
+// small copy kernel on the caller's stream (one queue, no copy-engine handoff).
+// An event per buffer guards its reuse until the copy has finished.
 struct Stager {
   static constexpr int kSlots = 8;
   struct Slot {
     void* host = nullptr;
+    void* mapped = nullptr;   // the same buffer as seen from the device
     size_t cap = 0;
     hipEvent_t ev = nullptr;
     bool pending = false;
@@ -370,18 +387,28 @@ hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t
     if (s.host && (e = hipHostFree(s.host)) != hipSuccess) return e;
     s.host = nullptr;
     size_t cap = std::max<size_t>(bytes, 64 * 1024);
-    if ((e = hipHostMalloc(&s.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
+    if ((e = hipHostMalloc(&s.host, cap, hipHostMallocMapped)) != hipSuccess) return e;
+    if ((e = hipHostGetDevicePointer(&s.mapped, s.host, 0)) != hipSuccess) return e;
     s.cap = cap;
   }
   if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
   std::memcpy(s.host, src, bytes);
-  if ((e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess) return e;
+  if (bytes % 16 == 0)
+    e = pk::launch_stage_copy(s.mapped, dst, bytes, stream);
+  else
+    e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
   if ((e = hipEventRecord(s.ev, stream)) != hipSuccess) return e;
   s.pending = true;
   return hipSuccess;
 }
 
 // ---- per-launch timing trace ------------------------------------------------------------
+// While tracing is on, every launch records start/stop events through its own dispatch packet.
+// Launches still in flight keep their events in g_pending; finished ones are turned into
+// records (and their events recycled) whenever a new launch is traced, so only a few dozen
+// events are ever live and none are created inside a timed loop once the pool is warm.
+
 enum TraceKernel { kTraceAppend = 0, kTraceVector = 1, kTraceMatrix = 2, kTraceMerge = 3 };
 
 struct TraceEntry {
@@ -392,9 +419,14 @@ struct TraceEntry {
 
 std::mutex g_trace_mu;
 bool g_trace_on = false;
-std::vector<TraceEntry> g_trace;
+int g_trace_every = 1;                // time every n-th launch of each kernel kind
+long long g_trace_seen[5] = {};       // launches per kernel kind since tracing was enabled
+std::deque<TraceEntry> g_pending;
+std::vector<pensieve_trace_record> g_records;
+hipError_t g_trace_error = hipSuccess;
 std::vector<hipEvent_t> g_event_pool;
 constexpr size_t kMaxTraceEntries = 1 << 16;
+constexpr size_t kTracePoolWarm = 256;
 
 hipEvent_t trace_event() {
   if (!g_event_pool.empty()) {
@@ -407,22 +439,45 @@ hipEvent_t trace_event() {
   return e;
 }
 
-// Brackets one kernel launch with events when tracing is on.
+// Turn one traced launch into a record and recycle its events (g_trace_mu held).
+void finish_entry(const TraceEntry& t) {
+  float ms = 0.f;
+  const hipError_t e = hipEventElapsedTime(&ms, t.start, t.stop);
+  if (e != hipSuccess && g_trace_error == hipSuccess) g_trace_error = e;
+  if (g_records.size() < kMaxTraceEntries) g_records.push_back({t.kernel, t.items, ms});
+  g_event_pool.push_back(t.start);
+  g_event_pool.push_back(t.stop);
+}
+
+// Collect the launches that have finished, oldest first (g_trace_mu held).
+void harvest_finished() {
+  while (!g_pending.empty() && hipEventQuery(g_pending.front().stop) == hipSuccess) {
+    finish_entry(g_pending.front());
+    g_pending.pop_front();
+  }
+}
+
+// Times the one launch made while it is alive: the launch itself records the events (its
+// dispatch packet carries them, hipExtLaunchKernel), so timing adds no packets to the stream.
 struct TraceScope {
   bool active = false;
   TraceEntry entry{};
-  hipStream_t stream;
-  TraceScope(int kernel, int items, hipStream_t s) : stream(s) {
+  TraceScope(int kernel, int items, hipStream_t) {
     std::lock_guard<std::mutex> lk(g_trace_mu);
-    if (!g_trace_on || g_trace.size() >= kMaxTraceEntries) return;
+    if (!g_trace_on) return;
+    if (g_trace_seen[kernel]++ % g_trace_every != 0) return;
+    harvest_finished();
+    if (g_records.size() + g_pending.size() >= kMaxTraceEntries) return;
     entry = {kernel, items, trace_event(), trace_event()};
     if (!entry.start || !entry.stop) return;
-    active = hipEventRecord(entry.start, stream) == hipSuccess;
+    pk::launch_events() = {entry.start, entry.stop};
+    active = true;
   }
   ~TraceScope() {
     if (!active) return;
+    pk::launch_events() = {};
     std::lock_guard<std::mutex> lk(g_trace_mu);
-    if (hipEventRecord(entry.stop, stream) == hipSuccess) g_trace.push_back(entry);
+    g_pending.push_back(entry);
   }
 };
 
@@ -593,7 +648,7 @@ pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, in
   if (!bytes) return fail(PENSIEVE_ERR_INVALID_ARG, "bytes is NULL");
   if (num_partitions < 0 || num_partitions > kMaxPartitions)
     return fail(PENSIEVE_ERR_INVALID_ARG, "num_partitions must be in [0, %d]", kMaxPartitions);
-  Plan plan;
+  thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, num_partitions, plan);
   *bytes = plan.bytes();
   return ok();
@@ -609,7 +664,7 @@ pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q
   if (total_q(desc) == 0) return ok();
   if (!o) return fail(PENSIEVE_ERR_INVALID_ARG, "o is NULL");
   if (o == q) return fail(PENSIEVE_ERR_INVALID_ARG, "o must not alias q");
-  Plan plan;
+  thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, 0, plan);
   if (!workspace || workspace_bytes < plan.bytes())
     return fail(PENSIEVE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes(),
@@ -633,7 +688,7 @@ pensieve_status pensieve_attn_split_partial(const pensieve_batch_desc* desc, int
   if ((s = check_attn_pointers(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens)) != PENSIEVE_OK) return s;
   if (total_q(desc) == 0) return ok();
   if (!part_o || !part_m || !part_l) return fail(PENSIEVE_ERR_INVALID_ARG, "a partial buffer is NULL");
-  Plan plan;
+  thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, num_partitions, plan);
   if (!workspace || workspace_bytes < plan.bytes())
     return fail(PENSIEVE_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", plan.bytes(),
@@ -673,7 +728,7 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
   if (num_partitions < 0 || num_partitions > kMaxPartitions)
     return fail(PENSIEVE_ERR_INVALID_ARG, "num_partitions must be in [0, %d]", kMaxPartitions);
   if (!num_items || (max_items > 0 && !items_host)) return fail(PENSIEVE_ERR_INVALID_ARG, "NULL output");
-  Plan plan;
+  thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, num_partitions, plan);
   *num_items = (int32_t)plan.planned.size();
   for (int i = 0; i < (int)plan.planned.size() && i < max_items; ++i) {
@@ -695,34 +750,34 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
 
 pensieve_status pensieve_trace_enable(int32_t enable) {
   std::lock_guard<std::mutex> lk(g_trace_mu);
-  g_trace_on = enable != 0;
+  g_trace_on = enable > 0;
+  g_trace_every = enable > 0 ? enable : 1;
+  for (long long& n : g_trace_seen) n = 0;
+  // Warm the event pool now, so that a timed loop traced from here on creates none.
+  while (g_trace_on && g_event_pool.size() < kTracePoolWarm) {
+    hipEvent_t e = nullptr;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_fail(err, "trace event pool");
+    g_event_pool.push_back(e);
+  }
   return ok();
 }
 
 pensieve_status pensieve_trace_read(pensieve_trace_record* records_host, int32_t max_records, int32_t* num_records) {
   if (!num_records || (max_records > 0 && !records_host)) return fail(PENSIEVE_ERR_INVALID_ARG, "NULL output");
-  std::vector<TraceEntry> entries;
-  {
-    std::lock_guard<std::mutex> lk(g_trace_mu);
-    entries.swap(g_trace);
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  while (!g_pending.empty()) {
+    const hipError_t e = hipEventSynchronize(g_pending.front().stop);
+    if (e != hipSuccess && g_trace_error == hipSuccess) g_trace_error = e;
+    finish_entry(g_pending.front());
+    g_pending.pop_front();
   }
-  int32_t n = 0;
-  hipError_t err = hipSuccess;
-  for (const TraceEntry& t : entries) {
-    float ms = 0.f;
-    hipError_t e = hipEventSynchronize(t.stop);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
-    if (e != hipSuccess && err == hipSuccess) err = e;
-    if (n < max_records) records_host[n++] = {t.kernel, t.items, ms};
-  }
-  {
-    std::lock_guard<std::mutex> lk(g_trace_mu);
-    for (const TraceEntry& t : entries) {
-      g_event_pool.push_back(t.start);
-      g_event_pool.push_back(t.stop);
-    }
-  }
+  const int32_t n = (int32_t)std::min<size_t>(g_records.size(), (size_t)std::max(0, max_records));
+  if (n > 0) std::memcpy(records_host, g_records.data(), n * sizeof(pensieve_trace_record));
+  g_records.clear();
   *num_records = n;
+  const hipError_t err = g_trace_error;
+  g_trace_error = hipSuccess;
   if (err != hipSuccess) return hip_fail(err, "trace read");
   return ok();
 }

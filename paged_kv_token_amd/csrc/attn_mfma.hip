@@ -467,12 +467,12 @@ template <int DT, int D>
 static hipError_t launch_mfma_d(const AttnArgs& args, int group, hipStream_t stream) {
   dim3 grid(args.num_items), block(256);
   switch (group) {
-    case 1: hipLaunchKernelGGL((attn_mfma_kernel<DT, D, 1>), grid, block, 0, stream, args); break;
-    case 2: hipLaunchKernelGGL((attn_mfma_kernel<DT, D, 2>), grid, block, 0, stream, args); break;
-    case 4: hipLaunchKernelGGL((attn_mfma_kernel<DT, D, 4>), grid, block, 0, stream, args); break;
-    case 8: hipLaunchKernelGGL((attn_mfma_kernel<DT, D, 8>), grid, block, 0, stream, args); break;
-    case 16: hipLaunchKernelGGL((attn_mfma_kernel<DT, D, 16>), grid, block, 0, stream, args); break;
-    case 32: hipLaunchKernelGGL((attn_mfma_kernel<DT, D, 32>), grid, block, 0, stream, args); break;
+    case 1: PK_LAUNCH((attn_mfma_kernel<DT, D, 1>), grid, block, stream, args); break;
+    case 2: PK_LAUNCH((attn_mfma_kernel<DT, D, 2>), grid, block, stream, args); break;
+    case 4: PK_LAUNCH((attn_mfma_kernel<DT, D, 4>), grid, block, stream, args); break;
+    case 8: PK_LAUNCH((attn_mfma_kernel<DT, D, 8>), grid, block, stream, args); break;
+    case 16: PK_LAUNCH((attn_mfma_kernel<DT, D, 16>), grid, block, stream, args); break;
+    case 32: PK_LAUNCH((attn_mfma_kernel<DT, D, 32>), grid, block, stream, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

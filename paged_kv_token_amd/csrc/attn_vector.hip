@@ -237,10 +237,10 @@ template <int DT, int D>
 static hipError_t launch_vec_d(const AttnArgs& args, int rows, hipStream_t stream) {
   dim3 grid(args.num_items), block(256);
   switch (rows) {
-    case 1: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 1>), grid, block, 0, stream, args); break;
-    case 2: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 2>), grid, block, 0, stream, args); break;
-    case 4: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 4>), grid, block, 0, stream, args); break;
-    default: hipLaunchKernelGGL((attn_vector_kernel<DT, D, 8>), grid, block, 0, stream, args); break;
+    case 1: PK_LAUNCH((attn_vector_kernel<DT, D, 1>), grid, block, stream, args); break;
+    case 2: PK_LAUNCH((attn_vector_kernel<DT, D, 2>), grid, block, stream, args); break;
+    case 4: PK_LAUNCH((attn_vector_kernel<DT, D, 4>), grid, block, stream, args); break;
+    default: PK_LAUNCH((attn_vector_kernel<DT, D, 8>), grid, block, stream, args); break;
   }
   return hipGetLastError();
 }

@@ -92,7 +92,7 @@ template <int EB, int D>
 static hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                                 const int32_t* slots, int num_tokens, int num_kv_heads, hipStream_t stream) {
   dim3 grid((num_tokens + 15) / 16, num_kv_heads);
-  hipLaunchKernelGGL((kv_append_kernel<EB, D>), grid, dim3(256), 0, stream,
+  PK_LAUNCH((kv_append_kernel<EB, D>), grid, dim3(256), stream,
                      static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
                      static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slots, num_tokens,
                      num_kv_heads);

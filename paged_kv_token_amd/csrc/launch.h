@@ -1,12 +1,32 @@
 // Host-side launchers of the gfx950 kernels (one per kernel family).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "device_common.h"
 
 namespace pk {
+
+// Events the next kernel launch on this host thread records its start and end time into
+// (through the dispatch packet itself, hipExtLaunchKernel); both null when not timing.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+// Launch a kernel on `stream`, timed into launch_events() when they are set (an ordinary
+// launch otherwise).
+#define PK_LAUNCH(KERNEL, GRID, BLOCK, STREAM, ...)                                                 \
+  do {                                                                                             \
+    const ::pk::LaunchEvents& pk_ev_ = ::pk::launch_events();                                      \
+    if (pk_ev_.start)                                                                              \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, pk_ev_.start, pk_ev_.stop, 0, __VA_ARGS__); \
+    else                                                                                           \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, STREAM, __VA_ARGS__);                             \
+  } while (0)
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                             const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
@@ -20,6 +40,10 @@ hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int head_dim, int
 // Matrix-core attention: items of up to 128 query vectors (tokens x the
 // whole head group), fp16/bf16 only.
 hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int head_dim, int group, hipStream_t stream);
+
+// Copy `bytes` (a multiple of 16) from a device-mapped page-locked host buffer to device
+// memory with a kernel on `stream`.
+hipError_t launch_stage_copy(const void* src_mapped, void* dst, size_t bytes, hipStream_t stream);
 
 // Merge of split partials into O: rows = partial rows x num_heads; rowmap
 // (nullable) gives each partial row's output row and partition count.

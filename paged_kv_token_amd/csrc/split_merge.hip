@@ -77,10 +77,10 @@ static hipError_t launch_merge_dt(const float* po, const float* pm, const float*
                                   int head_dim, int P, const int32_t* rowmap, void* o, hipStream_t stream) {
   dim3 grid((rows + 3) / 4), block(256);
   if (head_dim == 64)
-    hipLaunchKernelGGL((split_merge_kernel<DT, 64>), grid, block, 0, stream, po, pm, pl, rows, num_heads, P, rowmap,
+    PK_LAUNCH((split_merge_kernel<DT, 64>), grid, block, stream, po, pm, pl, rows, num_heads, P, rowmap,
                        (uint8_t*)o);
   else
-    hipLaunchKernelGGL((split_merge_kernel<DT, 128>), grid, block, 0, stream, po, pm, pl, rows, num_heads, P, rowmap,
+    PK_LAUNCH((split_merge_kernel<DT, 128>), grid, block, stream, po, pm, pl, rows, num_heads, P, rowmap,
                        (uint8_t*)o);
   return hipGetLastError();
 }
