@@ -369,6 +369,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-hbm-copy", action="store_true", help="skip the device-copy bandwidth measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (a reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -419,7 +420,7 @@ def main():
                             "hbm_frac": round(total_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del dev
     torch.cuda.empty_cache()
-    result["hbm_copy"] = copy_bandwidth()
+    result["hbm_copy"] = None if args.no_hbm_copy else copy_bandwidth()
     if not args.no_secondary:
         result["secondary"] = []
         for idx in (2, 3, 4):
