@@ -292,6 +292,66 @@ def copy_bandwidth(mib: int = 1024, reps: int = 10):
             "what": f"{mib} MiB device-to-device copy, bytes read + written"}
 
 
+def swap_measure(index: int = 1, reps: int = 5, steps: int = 40):
+    """Block swap with a pinned host tier on one workload: every block the batch uses goes out and
+    comes back (GB/s each way over the host link); then attention steps run alone, and again with a
+    swap-in on a second stream in every step (into spare device blocks) of as many blocks as the
+    link carries in half a step: the swap should hide behind the attention."""
+    import torch
+    b = config_batch(index)
+    dev = DeviceBatch(b, copies=1)
+    used = b.used_blocks().astype(np.int32)
+    n = len(used)
+    k_host = torch.empty((n,) + tuple(dev.k_pool.shape[1:]), dtype=dev.k_pool.dtype).pin_memory()
+    v_host = torch.empty((n,) + tuple(dev.v_pool.shape[1:]), dtype=dev.v_pool.dtype).pin_memory()
+    host_ids = np.arange(n, dtype=np.int32)
+    nbytes = 2 * n * b.num_kv_heads * 16 * b.head_dim * b.elem_bytes
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    out_ms = timed(lambda: pk.pensieve_kv_swap_out(dev.k_pool, dev.v_pool, k_host, v_host, used, host_ids))
+    in_ms = timed(lambda: pk.pensieve_kv_swap_in(dev.k_pool, dev.v_pool, k_host, v_host, host_ids, used))
+    spare = np.setdiff1d(np.arange(b.num_blocks), used).astype(np.int32)
+    side = torch.cuda.Stream()
+    block_bytes = 2 * b.num_kv_heads * 16 * b.head_dim * b.elem_bytes
+
+    def steps_ms(m):
+        """Wall time per step, both streams drained at the end."""
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(steps):
+            if m:
+                with torch.cuda.stream(side):
+                    pk.pensieve_kv_swap_in(dev.k_pool, dev.v_pool, k_host, v_host, host_ids[:m], spare[:m],
+                                           stream=side)
+            dev.attn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - w0) * 1e3 / steps
+
+    steps_ms(0)
+    alone = steps_ms(0)
+    m = int(min(len(spare), 0.5 * alone * 1e-3 * (nbytes / (in_ms * 1e-3)) / block_bytes))
+    beside = steps_ms(m)
+    m_bytes = m * block_bytes
+    out = {"workload": b.name, "blocks": n, "bytes": nbytes, "swap_out_ms": round(out_ms, 3),
+           "swap_out_gbs": round(nbytes / (out_ms * 1e-3) / 1e9, 1), "swap_in_ms": round(in_ms, 3),
+           "swap_in_gbs": round(nbytes / (in_ms * 1e-3) / 1e9, 1),
+           "overlap": {"step_ms_alone": round(alone, 4), "step_ms_with_swap_in": round(beside, 4),
+                       "swap_in_blocks_per_step": m, "swap_in_bytes_per_step": m_bytes}}
+    del dev, k_host, v_host
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -421,6 +481,9 @@ def main():
     del dev
     torch.cuda.empty_cache()
     result["hbm_copy"] = None if args.no_hbm_copy else copy_bandwidth()
+    if not args.no_secondary:
+        log("block swap with a pinned host tier")
+        result["kv_swap"] = swap_measure()
     if not args.no_secondary:
         result["secondary"] = []
         for idx in (2, 3, 4):

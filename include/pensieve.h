@@ -120,6 +120,34 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
                                    int32_t num_blocks, int32_t dtype, void* stream);
 
 /*
+ * Block swap with a host tier ("Stateful Large Language Model Serving with
+ * Pensieve", Methodology and AI Executive Summary: cached KV tokens move
+ * between a GPU tier and a CPU tier, swapped ahead of time with transfers
+ * pipelined behind computation).  The host tier k_host/v_host has the pools'
+ * block layout ([num_host_blocks][Hkv][16][d] and [num_host_blocks][Hkv][d][16])
+ * and must be page-locked host memory mapped for the device (hipHostMalloc,
+ * or a pinned torch tensor).  A swap copies n whole blocks, every KV head:
+ *   pensieve_kv_swap_out: host block host_blocks[i] = device block device_blocks[i]
+ *   pensieve_kv_swap_in:  device block device_blocks[i] = host block host_blocks[i]
+ * The block lists are host arrays of n int32, read before the call returns;
+ * every id must lie in its pool and destinations must be distinct
+ * (INVALID_ARG otherwise, before anything is enqueued).  The copy is
+ * bit-exact and asynchronous on `stream`: run a swap-in on a second stream
+ * beside the current step's attention, and make the step that reads the
+ * blocks wait for it (an event).  Nothing else in either tier changes.
+ */
+pensieve_status pensieve_kv_swap_out(void* k_pool, void* v_pool, int32_t num_blocks, void* k_host,
+                                     void* v_host, int32_t num_host_blocks,
+                                     const int32_t* device_blocks_host, const int32_t* host_blocks_host,
+                                     int32_t n, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                     void* stream);
+pensieve_status pensieve_kv_swap_in(void* k_pool, void* v_pool, int32_t num_blocks, void* k_host,
+                                    void* v_host, int32_t num_host_blocks,
+                                    const int32_t* host_blocks_host, const int32_t* device_blocks_host,
+                                    int32_t n, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                    void* stream);
+
+/*
  * Workspace needed by pensieve_attn_fwd (num_partitions == 0) or by
  * pensieve_attn_split_partial (num_partitions >= 1) for this batch.  The
  * workspace holds the device copy of the work list and, when
@@ -199,7 +227,8 @@ pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num
  * pensieve_trace_read waits for the traced launches still in flight,
  * writes up to max_records records {kernel, work items, milliseconds} in
  * launch order (kernel: 0 kv_append, 1 vector attention, 2 matrix-core
- * attention, 3 split merge), sets *num_records to the number written, and
+ * attention, 3 split merge, 4 block swap), sets *num_records to the number
+ * written, and
  * clears the trace (at most 65536 records are kept between reads).
  * enable > 0 turns tracing on and times every enable-th launch of each kernel
  * kind (1: every launch); 0 turns it off.  A timed launch costs more than an

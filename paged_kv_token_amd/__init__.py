@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     pensieve_attn_workspace_size,
     pensieve_debug_plan,
     pensieve_kv_append,
+    pensieve_kv_swap_in,
+    pensieve_kv_swap_out,
     pensieve_trace_enable,
     pensieve_trace_read,
     pensieve_version,

@@ -29,9 +29,9 @@ PENSIEVE_FLAG_VECTOR_ONLY = 1
 EXPORTED = (
     "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",
     "pensieve_attn_fwd", "pensieve_attn_split_partial", "pensieve_attn_split_merge", "pensieve_debug_plan",
-    "pensieve_trace_enable", "pensieve_trace_read",
+    "pensieve_trace_enable", "pensieve_trace_read", "pensieve_kv_swap_out", "pensieve_kv_swap_in",
 )
-TRACE_KERNELS = {0: "kv_append", 1: "attn_vector", 2: "attn_mfma", 3: "split_merge"}
+TRACE_KERNELS = {0: "kv_append", 1: "attn_vector", 2: "attn_mfma", 3: "split_merge", 4: "kv_swap"}
 
 
 class PensieveError(RuntimeError):
@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None):
     lib.pensieve_version.restype = ctypes.c_char_p
     lib.pensieve_last_error.restype = ctypes.c_char_p
     lib.pensieve_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pensieve_kv_swap_out.argtypes = [vp, vp, i32, vp, vp, i32, i32p, i32p, i32, i32, i32, i32, vp]
+    lib.pensieve_kv_swap_in.argtypes = [vp, vp, i32, vp, vp, i32, i32p, i32p, i32, i32, i32, i32, vp]
     lib.pensieve_attn_workspace_size.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.pensieve_attn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.pensieve_attn_split_partial.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -159,6 +161,42 @@ def pensieve_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None):
                                   _ptr(k_pool, "k_pool", k_new.dtype), _ptr(v_pool, "v_pool", k_new.dtype),
                                   _ptr(slot_mapping, "slot_mapping", torch.int32), n, hkv, d, k_pool.shape[2], nb,
                                   dtype_code(k_new), _stream(stream)))
+
+
+def _host_ptr(t, name: str, dtype):
+    """A host tensor; the library itself checks that it is page-locked and mapped for the device."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise ValueError(f"{name} must be a pinned host tensor")
+    if not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name} must be contiguous {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _block_list(blocks):
+    arr = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32).reshape(-1))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _kv_swap(fn, k_pool, v_pool, k_host, v_host, first, second, stream):
+    k_arr, k_p = _block_list(first)
+    s_arr, s_p = _block_list(second)
+    if len(k_arr) != len(s_arr):
+        raise ValueError("block lists differ in length")
+    _, hkv, _, d = k_pool.shape
+    _check(fn(_ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype), k_pool.shape[0],
+              _host_ptr(k_host, "k_host", k_pool.dtype), _host_ptr(v_host, "v_host", k_pool.dtype), k_host.shape[0],
+              k_p, s_p, len(k_arr), hkv, d, dtype_code(k_pool), _stream(stream)))
+
+
+def pensieve_kv_swap_out(k_pool, v_pool, k_host, v_host, device_blocks, host_blocks, stream=None):
+    """Copy device blocks device_blocks[i] of the pools to host blocks host_blocks[i] of the pinned host tier."""
+    _kv_swap(load_library().pensieve_kv_swap_out, k_pool, v_pool, k_host, v_host, device_blocks, host_blocks, stream)
+
+
+def pensieve_kv_swap_in(k_pool, v_pool, k_host, v_host, host_blocks, device_blocks, stream=None):
+    """Copy host blocks host_blocks[i] of the pinned host tier to device blocks device_blocks[i] of the pools."""
+    _kv_swap(load_library().pensieve_kv_swap_in, k_pool, v_pool, k_host, v_host, host_blocks, device_blocks, stream)
 
 
 def pensieve_attn_workspace_size(desc: BatchDesc, num_partitions: int = 0) -> int:

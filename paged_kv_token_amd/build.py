@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpensieve.so")
 
-SOURCES = ["api.cpp", "kv_append.hip", "attn_vector.hip", "attn_mfma.hip", "split_merge.hip", "stage_copy.hip"]
+SOURCES = ["api.cpp", "kv_append.hip", "attn_vector.hip", "attn_mfma.hip", "split_merge.hip", "stage_copy.hip", "kv_swap.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

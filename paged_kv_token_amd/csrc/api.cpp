@@ -343,7 +343,7 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
 // small copy kernel on the caller's stream (one queue, no copy-engine handoff).
 // An event per buffer guards its reuse until the copy has finished.
 struct Stager {
-  static constexpr int kSlots = 8;
+  static constexpr int kSlots = 32;   // deep enough that a long swap does not hold up later calls
   struct Slot {
     void* host = nullptr;
     void* mapped = nullptr;   // the same buffer as seen from the device
@@ -371,8 +371,10 @@ Stager* stager_for_current_device(hipError_t* err) {
   return s;
 }
 
-hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  if (bytes == 0) return hipSuccess;
+// Copy `bytes` from `src` into the next staging buffer of this device (waiting until the
+// buffer's previous use on the GPU has finished) and return its device mapping; the caller
+// enqueues the work that reads it, then calls stage_release on the same stream.
+hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::Slot** slot_out) {
   hipError_t e;
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
@@ -393,14 +395,34 @@ hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t
   }
   if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
   std::memcpy(s.host, src, bytes);
-  if (bytes % 16 == 0)
-    e = pk::launch_stage_copy(s.mapped, dst, bytes, stream);
-  else
-    e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(s.ev, stream)) != hipSuccess) return e;
-  s.pending = true;
+  *mapped = s.mapped;
+  *slot_out = &s;
   return hipSuccess;
+}
+
+// The staging buffer may be reused once the stream has passed this point.
+hipError_t stage_release(Stager::Slot* slot, hipStream_t stream) {
+  hipError_t e;
+  Stager* st = stager_for_current_device(&e);
+  if (!st) return e;
+  std::lock_guard<std::mutex> lk(st->mu);
+  if ((e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
+  slot->pending = true;
+  return hipSuccess;
+}
+
+hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  void* mapped = nullptr;
+  Stager::Slot* slot = nullptr;
+  hipError_t e = stage_acquire(src, bytes, &mapped, &slot);
+  if (e != hipSuccess) return e;
+  if (bytes % 16 == 0)
+    e = pk::launch_stage_copy(mapped, dst, bytes, stream);
+  else
+    e = hipMemcpyAsync(dst, slot->host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
+  return stage_release(slot, stream);
 }
 
 // ---- per-launch timing trace ------------------------------------------------------------
@@ -409,7 +431,7 @@ hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t
 // records (and their events recycled) whenever a new launch is traced, so only a few dozen
 // events are ever live and none are created inside a timed loop once the pool is warm.
 
-enum TraceKernel { kTraceAppend = 0, kTraceVector = 1, kTraceMatrix = 2, kTraceMerge = 3 };
+enum TraceKernel { kTraceAppend = 0, kTraceVector = 1, kTraceMatrix = 2, kTraceMerge = 3, kTraceSwap = 4 };
 
 struct TraceEntry {
   int kernel;
@@ -420,7 +442,7 @@ struct TraceEntry {
 std::mutex g_trace_mu;
 bool g_trace_on = false;
 int g_trace_every = 1;                // time every n-th launch of each kernel kind
-long long g_trace_seen[5] = {};       // launches per kernel kind since tracing was enabled
+long long g_trace_seen[5] = {};  // indexed by TraceKernel       // launches per kernel kind since tracing was enabled
 std::deque<TraceEntry> g_pending;
 std::vector<pensieve_trace_record> g_records;
 hipError_t g_trace_error = hipSuccess;
@@ -613,9 +635,83 @@ pensieve_status check_attn_pointers(const pensieve_batch_desc* d, const void* q,
   return PENSIEVE_OK;
 }
 
+// Device address of page-locked host memory (hipHostMalloc / pinned allocations), or null.
+void* mapped_host_pointer(void* host) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost) return nullptr;
+  return attr.devicePointer;
+}
+
+pensieve_status kv_swap(bool to_host, void* k_pool, void* v_pool, int32_t num_blocks, void* k_host, void* v_host,
+                        int32_t num_host_blocks, const int32_t* src_blocks_host, const int32_t* dst_blocks_host,
+                        int32_t n, int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* stream) {
+  if (n < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "n < 0");
+  if (num_kv_heads <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+  if (head_dim != 64 && head_dim != 128) return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported", head_dim);
+  if (!valid_dtype(dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (num_blocks <= 0 || num_host_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "pool sizes must be > 0");
+  if (n == 0) return ok();
+  if (!k_pool || !v_pool || !k_host || !v_host) return fail(PENSIEVE_ERR_INVALID_ARG, "a pool pointer is NULL");
+  if (!src_blocks_host || !dst_blocks_host) return fail(PENSIEVE_ERR_INVALID_ARG, "a block list is NULL");
+  const int32_t n_src = to_host ? num_blocks : num_host_blocks;
+  const int32_t n_dst = to_host ? num_host_blocks : num_blocks;
+  std::vector<int32_t> pairs(2 * (size_t)n);
+  std::vector<uint8_t> taken(n_dst, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t sb = src_blocks_host[i], db = dst_blocks_host[i];
+    if (sb < 0 || sb >= n_src) return fail(PENSIEVE_ERR_INVALID_ARG, "source block %d at %d out of range", sb, i);
+    if (db < 0 || db >= n_dst) return fail(PENSIEVE_ERR_INVALID_ARG, "destination block %d at %d out of range", db, i);
+    if (taken[db]) return fail(PENSIEVE_ERR_INVALID_ARG, "destination block %d appears twice", db);
+    taken[db] = 1;
+    pairs[2 * i] = sb;
+    pairs[2 * i + 1] = db;
+  }
+  void* k_map = mapped_host_pointer(k_host);
+  void* v_map = mapped_host_pointer(v_host);
+  if (!k_map || !v_map)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "k_host / v_host must be page-locked host memory mapped for the device");
+  const int64_t block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  void* pairs_map = nullptr;
+  Stager::Slot* slot = nullptr;
+  hipError_t e = stage_acquire(pairs.data(), pairs.size() * sizeof(int32_t), &pairs_map, &slot);
+  if (e != hipSuccess) return hip_fail(e, "block list staging");
+  {
+    TraceScope trace(kTraceSwap, n, st);
+    e = to_host ? pk::launch_kv_swap(k_pool, v_pool, k_map, v_map, static_cast<const int32_t*>(pairs_map), n,
+                                     block_bytes, st)
+                : pk::launch_kv_swap(k_map, v_map, k_pool, v_pool, static_cast<const int32_t*>(pairs_map), n,
+                                     block_bytes, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "kv swap launch");
+  if ((e = stage_release(slot, st)) != hipSuccess) return hip_fail(e, "block list staging");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+pensieve_status pensieve_kv_swap_out(void* k_pool, void* v_pool, int32_t num_blocks, void* k_host, void* v_host,
+                                     int32_t num_host_blocks, const int32_t* device_blocks_host,
+                                     const int32_t* host_blocks_host, int32_t n, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t dtype, void* stream) {
+  return kv_swap(true, k_pool, v_pool, num_blocks, k_host, v_host, num_host_blocks, device_blocks_host,
+                 host_blocks_host, n, num_kv_heads, head_dim, dtype, stream);
+}
+
+pensieve_status pensieve_kv_swap_in(void* k_pool, void* v_pool, int32_t num_blocks, void* k_host, void* v_host,
+                                    int32_t num_host_blocks, const int32_t* host_blocks_host,
+                                    const int32_t* device_blocks_host, int32_t n, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t dtype, void* stream) {
+  return kv_swap(false, k_pool, v_pool, num_blocks, k_host, v_host, num_host_blocks, host_blocks_host,
+                 device_blocks_host, n, num_kv_heads, head_dim, dtype, stream);
+}
+
 
 const char* pensieve_version(void) { return "pensieve 0.1 gfx950"; }
 

@@ -41,6 +41,11 @@ hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int head_dim, int
 // whole head group), fp16/bf16 only.
 hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int head_dim, int group, hipStream_t stream);
 
+// Copy n whole blocks (K and V runs of block_bytes each) from src to dst pools; pairs holds n
+// {source block, destination block} pairs.  Either side may be device-mapped host memory.
+hipError_t launch_kv_swap(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int32_t* pairs,
+                          int n, int64_t block_bytes, hipStream_t stream);
+
 // Copy `bytes` (a multiple of 16) from a device-mapped page-locked host buffer to device
 // memory with a kernel on `stream`.
 hipError_t launch_stage_copy(const void* src_mapped, void* dst, size_t bytes, hipStream_t stream);

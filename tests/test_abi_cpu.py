@@ -194,3 +194,55 @@ def test_workspace_size_matches_plan(lib):
     n = len(pk.pensieve_debug_plan(d))
     ws = pk.pensieve_attn_workspace_size(d)
     assert ws >= 32 * n and ws % 256 == 0 and ws < 32 * n + 256
+
+
+def _swap_args(n, src, dst, **over):
+    a = dict(k_pool=ctypes.c_void_p(0x1000), v_pool=ctypes.c_void_p(0x2000), num_blocks=64,
+             k_host=ctypes.c_void_p(0x3000), v_host=ctypes.c_void_p(0x4000), num_host_blocks=32,
+             n=n, num_kv_heads=4, head_dim=64, dtype=1)
+    a.update(over)
+    s = (ctypes.c_int32 * max(1, n))(*src)
+    d = (ctypes.c_int32 * max(1, n))(*dst)
+    return a, s, d
+
+
+@pytest.mark.parametrize("direction", ["out", "in"])
+@pytest.mark.parametrize("case,status", [
+    ("src_out_of_range", 1), ("dst_out_of_range", 1), ("negative_id", 1), ("duplicate_destination", 1),
+    ("bad_head_dim", 2), ("bad_dtype", 2), ("null_pool", 1), ("null_list", 1), ("negative_n", 1),
+])
+def test_kv_swap_rejects_bad_arguments_before_any_launch(lib, direction, case, status):
+    """Block ids are checked against their own pool on the host (device pools have 64 blocks, the
+    host tier 32), so a bad list never reaches a kernel; the fake pool pointers are never touched."""
+    out = direction == "out"
+    n_src, n_dst = (64, 32) if out else (32, 64)
+    src, dst = [0, 5, 7], [1, 2, 3]
+    over = {}
+    if case == "src_out_of_range":
+        src = [0, n_src, 1]
+    elif case == "dst_out_of_range":
+        dst = [0, n_dst, 1]
+    elif case == "negative_id":
+        src = [0, -1, 2]
+    elif case == "duplicate_destination":
+        dst = [4, 9, 4]
+    elif case == "bad_head_dim":
+        over["head_dim"] = 96
+    elif case == "bad_dtype":
+        over["dtype"] = 7
+    elif case == "null_pool":
+        over["k_pool"] = None
+    a, s, d = _swap_args(3, src, dst, **over)
+    if case == "null_list":
+        s = None
+    if case == "negative_n":
+        a["n"] = -1
+    fn = lib.pensieve_kv_swap_out if out else lib.pensieve_kv_swap_in
+    st = fn(a["k_pool"], a["v_pool"], a["num_blocks"], a["k_host"], a["v_host"], a["num_host_blocks"], s, d, a["n"],
+            a["num_kv_heads"], a["head_dim"], a["dtype"], None)
+    assert st == status
+    assert lib.pensieve_last_error().decode()
+
+
+def test_kv_swap_of_nothing_is_a_no_op(lib):
+    assert lib.pensieve_kv_swap_in(None, None, 1, None, None, 1, None, None, 0, 4, 64, 1, None) == 0
