@@ -148,6 +148,83 @@ pensieve_status pensieve_kv_swap_in(void* k_pool, void* v_pool, int32_t num_bloc
                                     void* stream);
 
 /*
+ * Cache planning for one serving step (host only: no device work, no stream).
+ * "Stateful Large Language Model Serving with Pensieve", Methodology: cached
+ * KV is dropped block by block, weighing a conversation's activity against
+ * the cost of recomputing what is dropped, and dropped tokens are recomputed
+ * with the conversation's next turn.
+ *
+ * A conversation is described by pensieve_conversation:
+ *   cached_tokens   positions 0..cached_tokens-1 were computed earlier; their
+ *                   KV sits in logical blocks 0..ceil(cached_tokens/16)-1
+ *   dropped_blocks  leading logical blocks 0..dropped_blocks-1 no longer hold
+ *                   KV on the device (their physical blocks were given back);
+ *                   at most ceil(cached_tokens/16)
+ *   new_tokens      tokens this step brings (0: not scheduled this step)
+ *   activity        weight >= 0 of keeping the conversation's cache (e.g. the
+ *                   inverse of its idle time); how it is measured is the
+ *                   caller's policy
+ */
+typedef struct pensieve_conversation {
+  int32_t cached_tokens;
+  int32_t dropped_blocks;
+  int32_t new_tokens;
+  float activity;
+} pensieve_conversation;
+
+/*
+ * Choose which blocks to drop so that the step fits in free_blocks.  The step
+ * takes, per scheduled conversation, dropped_blocks fresh blocks for its
+ * recomputed leading blocks plus the logical blocks its new tokens open.
+ * When that exceeds free_blocks, blocks of UNSCHEDULED conversations are
+ * dropped one at a time, leading resident block first, always the one of
+ * least cost activity * (j + 1) for logical block j (a block's recompute cost
+ * grows with the context it attends over; ties go to the lower conversation
+ * index) -- the least-cost set of that many leading-first drops.
+ * evict_blocks_host[c] receives how many more leading blocks conversation c
+ * drops (its logical blocks dropped_blocks .. dropped_blocks+evict-1; the
+ * caller frees them and adds evict to dropped_blocks); *freed_blocks their
+ * sum.  UNSUPPORTED when even dropping every unscheduled block is not enough
+ * (the outputs then hold that maximal drop).
+ */
+pensieve_status pensieve_cache_plan_evictions(const pensieve_conversation* conversations, int32_t n,
+                                              int32_t free_blocks, int32_t* evict_blocks_host,
+                                              int32_t* freed_blocks);
+
+/*
+ * Build the unified batch of one step from the scheduled conversations
+ * (new_tokens > 0), in conversation order: request r serves conversation
+ * request_conv_host[r].  Its query rows are the recompute rows -- every
+ * position of its dropped blocks, 0 .. min(16*dropped_blocks, cached_tokens)-1
+ * -- followed by its new rows cached_tokens .. cached_tokens+new_tokens-1;
+ * q_pos_host gives each row's position (strictly increasing in a request),
+ * context_lens_host[r] = cached_tokens + new_tokens.  Fresh physical blocks
+ * are taken from free_list_host in order: first for the dropped logical blocks
+ * 0..dropped_blocks-1, then for the logical blocks the new tokens open.
+ * block_tables_host [n][block_table_stride] (conversation rows) is updated in
+ * place with them and copied, per request, into req_block_tables_host
+ * [num_reqs][block_table_stride]; slot_mapping_host gives each row's append
+ * slot (feed it to pensieve_kv_append with the rows' recomputed and new K/V,
+ * and q_pos_host, cu_q_lens_host, context_lens_host and req_block_tables_host
+ * to pensieve_attn_fwd).  After the step the caller sets cached_tokens +=
+ * new_tokens and dropped_blocks = 0.
+ *   *num_reqs, *total_rows, *blocks_used   sizes of the batch (always written)
+ *   max_rows < 0: sizes only, no other output is touched; otherwise the row
+ *   arrays hold max_rows entries, cu_q_lens_host num_reqs+1, request_conv_host
+ *   and context_lens_host num_reqs.
+ * INVALID_ARG on inconsistent conversations, a block_table_stride too small
+ * for a scheduled conversation, too few rows or free blocks, before any
+ * output array is written.
+ */
+pensieve_status pensieve_cache_build_batch(const pensieve_conversation* conversations, int32_t n,
+                                           int32_t* block_tables_host, int32_t block_table_stride,
+                                           const int32_t* free_list_host, int32_t free_count, int32_t max_rows,
+                                           int32_t* num_reqs, int32_t* total_rows, int32_t* blocks_used,
+                                           int32_t* request_conv_host, int32_t* cu_q_lens_host,
+                                           int32_t* context_lens_host, int32_t* q_pos_host,
+                                           int32_t* slot_mapping_host, int32_t* req_block_tables_host);
+
+/*
  * Workspace needed by pensieve_attn_fwd (num_partitions == 0) or by
  * pensieve_attn_split_partial (num_partitions >= 1) for this batch.  The
  * workspace holds the device copy of the work list and, when

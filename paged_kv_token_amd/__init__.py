@@ -6,19 +6,25 @@ and a thin ctypes binding with the same entry-point names.
 """
 
 from .binding import (  # noqa: F401
+    CONVERSATION_DTYPE,
     BatchDesc,
     PensieveError,
     PENSIEVE_BF16,
+    PENSIEVE_ERR_INVALID_ARG,
+    PENSIEVE_ERR_UNSUPPORTED,
     PENSIEVE_F16,
     PENSIEVE_F32,
     PENSIEVE_FLAG_VECTOR_ONLY,
     dtype_code,
     load_library,
+    conversations,
     make_desc,
     pensieve_attn_fwd,
     pensieve_attn_split_merge,
     pensieve_attn_split_partial,
     pensieve_attn_workspace_size,
+    pensieve_cache_build_batch,
+    pensieve_cache_plan_evictions,
     pensieve_debug_plan,
     pensieve_kv_append,
     pensieve_kv_swap_in,

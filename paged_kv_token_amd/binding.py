@@ -30,6 +30,7 @@ EXPORTED = (
     "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",
     "pensieve_attn_fwd", "pensieve_attn_split_partial", "pensieve_attn_split_merge", "pensieve_debug_plan",
     "pensieve_trace_enable", "pensieve_trace_read", "pensieve_kv_swap_out", "pensieve_kv_swap_in",
+    "pensieve_cache_plan_evictions", "pensieve_cache_build_batch",
 )
 TRACE_KERNELS = {0: "kv_append", 1: "attn_vector", 2: "attn_mfma", 3: "split_merge", 4: "kv_swap"}
 
@@ -63,6 +64,10 @@ class TraceRecord(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("items", ctypes.c_int32), ("ms", ctypes.c_float)]
 
 
+# Mirror of pensieve_conversation (host planning calls).
+CONVERSATION_DTYPE = np.dtype([("cached_tokens", "<i4"), ("dropped_blocks", "<i4"), ("new_tokens", "<i4"),
+                               ("activity", "<f4")], align=True)
+
 _lib = None
 
 
@@ -90,6 +95,9 @@ def load_library(path: Optional[str] = None):
     lib.pensieve_debug_plan.argtypes = [dp, i32, i32p, i32, i32p]
     lib.pensieve_trace_enable.argtypes = [i32]
     lib.pensieve_trace_read.argtypes = [ctypes.POINTER(TraceRecord), i32, i32p]
+    lib.pensieve_cache_plan_evictions.argtypes = [vp, i32, i32, i32p, i32p]
+    lib.pensieve_cache_build_batch.argtypes = [vp, i32, i32p, i32, i32p, i32, i32, i32p, i32p, i32p,
+                                               i32p, i32p, i32p, i32p, i32p, i32p]
     for name in EXPORTED[2:]:
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -260,3 +268,71 @@ def pensieve_trace_read(max_records: int = 1 << 16):
     _check(load_library().pensieve_trace_read(buf, max_records, ctypes.byref(n)))
     return [(TRACE_KERNELS.get(buf[i].kernel, str(buf[i].kernel)), int(buf[i].items), float(buf[i].ms))
             for i in range(n.value)]
+
+
+# ---- host cache planning -----------------------------------------------------
+def conversations(cached_tokens, dropped_blocks, new_tokens, activity) -> np.ndarray:
+    """Array of pensieve_conversation records from per-conversation sequences."""
+    n = len(cached_tokens)
+    out = np.zeros(n, dtype=CONVERSATION_DTYPE)
+    out["cached_tokens"] = cached_tokens
+    out["dropped_blocks"] = dropped_blocks
+    out["new_tokens"] = new_tokens
+    out["activity"] = activity
+    return out
+
+
+def _conv_arg(convs):
+    if not isinstance(convs, np.ndarray) or convs.dtype != CONVERSATION_DTYPE or not convs.flags.c_contiguous:
+        raise TypeError("conversations must be a contiguous array of CONVERSATION_DTYPE records")
+    return ctypes.c_void_p(convs.ctypes.data if len(convs) else 0), len(convs)
+
+
+def _i32_out(n: int) -> np.ndarray:
+    return np.zeros(max(int(n), 0), dtype=np.int32)
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def pensieve_cache_plan_evictions(convs: np.ndarray, free_blocks: int):
+    """Leading blocks each conversation drops so the step fits: (evict[n] int32, total)."""
+    ptr, n = _conv_arg(convs)
+    evict = _i32_out(n)
+    freed = ctypes.c_int32(0)
+    _check(load_library().pensieve_cache_plan_evictions(ptr, n, int(free_blocks), _i32p(evict),
+                                                        ctypes.byref(freed)))
+    return evict, int(freed.value)
+
+
+def pensieve_cache_build_batch(convs: np.ndarray, block_tables: np.ndarray, free_list) -> dict:
+    """Unified batch of the scheduled conversations; updates block_tables [n][stride] in place.
+
+    Returns a dict of int32 arrays: request_conv, cu_q_lens, context_lens, q_pos,
+    slot_mapping, req_block_tables, and the int blocks_used.
+    """
+    ptr, n = _conv_arg(convs)
+    if (not isinstance(block_tables, np.ndarray) or block_tables.dtype != np.int32 or block_tables.ndim != 2
+            or not block_tables.flags.c_contiguous or not block_tables.flags.writeable
+            or block_tables.shape[0] != n):
+        raise TypeError("block_tables must be a writeable C-contiguous int32 array [n][stride]")
+    stride = int(block_tables.shape[1])
+    free = np.ascontiguousarray(free_list, dtype=np.int32)
+    lib = load_library()
+    reqs, rows, used = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    none = ctypes.POINTER(ctypes.c_int32)()
+    _check(lib.pensieve_cache_build_batch(ptr, n, _i32p(block_tables), stride, _i32p(free), len(free), -1,
+                                          ctypes.byref(reqs), ctypes.byref(rows), ctypes.byref(used),
+                                          none, none, none, none, none, none))
+    R, T = int(reqs.value), int(rows.value)
+    out = {"request_conv": _i32_out(R), "cu_q_lens": _i32_out(R + 1), "context_lens": _i32_out(R),
+           "q_pos": _i32_out(T), "slot_mapping": _i32_out(T),
+           "req_block_tables": np.zeros((R, stride), dtype=np.int32)}
+    _check(lib.pensieve_cache_build_batch(ptr, n, _i32p(block_tables), stride, _i32p(free), len(free), T,
+                                          ctypes.byref(reqs), ctypes.byref(rows), ctypes.byref(used),
+                                          _i32p(out["request_conv"]), _i32p(out["cu_q_lens"]),
+                                          _i32p(out["context_lens"]), _i32p(out["q_pos"]),
+                                          _i32p(out["slot_mapping"]), _i32p(out["req_block_tables"])))
+    out["blocks_used"] = int(used.value)
+    return out

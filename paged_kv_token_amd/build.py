@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpensieve.so")
 
-SOURCES = ["api.cpp", "kv_append.hip", "attn_vector.hip", "attn_mfma.hip", "split_merge.hip", "stage_copy.hip", "kv_swap.hip"]
+SOURCES = ["api.cpp", "kv_append.hip", "attn_vector.hip", "attn_mfma.hip", "split_merge.hip", "stage_copy.hip", "kv_swap.hip",
+           "cache_plan.cpp"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -20,6 +20,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "host_status.h"
 #include "launch.h"
 #include "pensieve.h"
 
@@ -693,6 +694,14 @@ pensieve_status kv_swap(bool to_host, void* k_pool, void* v_pool, int32_t num_bl
 }
 
 }  // namespace
+
+namespace pk {
+pensieve_status set_error(pensieve_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+pensieve_status clear_error() { return ok(); }
+}  // namespace pk
 
 extern "C" {
 

@@ -1,0 +1,186 @@
+"""Multi-step serving simulation over a bounded block pool (test infrastructure).
+
+Conversations follow a seeded script of turns (``workloads.conversation_script``).
+Each step the library's planner drops leading blocks of idle conversations
+until the step fits in the free blocks (pensieve_cache_plan_evictions), then
+builds the unified batch (pensieve_cache_build_batch): recompute rows for the
+dropped leading tokens ahead of the new rows, fresh blocks from the free list,
+append slots and query positions.  A backend appends the rows' K/V into the
+pools and runs the attention; the output of every row must equal plain causal
+attention over the conversation's whole, never-evicted K/V -- the property
+that makes dropping and recomputing cache invisible to the model.
+
+A token's K/V depends only on (conversation, position): the model is
+deterministic, so a recomputed token reproduces the K/V it had before.  Freed
+blocks are poisoned with NaN so a stale read shows up in the output.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+import paged_kv_token_amd as pk
+from workloads import conversation_script, custom_batch, draw_rows, storage_dtype
+
+BLOCK = 16
+_TAG_STEP_Q = 77
+
+
+@dataclass
+class SimStats:
+    steps: int = 0
+    rows: int = 0
+    recompute_rows: int = 0
+    dropped_blocks: int = 0
+    fully_dropped: int = 0
+    deferred: int = 0
+    max_err: float = 0.0
+    per_step: list = field(default_factory=list)
+
+
+class OracleBackend:
+    """Pools on the host, filled and read by the CPU oracle."""
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, dtype):
+        sd = storage_dtype(dtype)
+        fill = np.uint16(0x7FC0) if dtype == "bf16" else np.nan
+        self.dtype = dtype
+        self.fill = fill
+        self.k_pool = np.full((num_blocks, num_kv_heads, BLOCK, head_dim), fill, dtype=sd)
+        self.v_pool = np.full((num_blocks, num_kv_heads, head_dim, BLOCK), fill, dtype=sd)
+
+    def free(self, blocks):
+        self.k_pool[blocks] = self.fill
+        self.v_pool[blocks] = self.fill
+
+    def step(self, q, k_rows, v_rows, slots, block_tables, context_lens, cu_q_lens, q_pos, scale, num_heads):
+        oracle.append_kv(self.k_pool, self.v_pool, k_rows, v_rows, slots, BLOCK)
+        return oracle.paged_attention(q, self.k_pool, self.v_pool, block_tables, context_lens, cu_q_lens, q_pos,
+                                      scale, self.dtype)
+
+
+class GpuBackend:
+    """Pools on the GPU, filled by pensieve_kv_append and read by pensieve_attn_fwd."""
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, dtype):
+        import torch
+        from gpu_harness import torch_dtype
+        td = torch_dtype(dtype)
+        self.dtype = dtype
+        self.num_blocks = num_blocks
+        self.k_pool = torch.full((num_blocks, num_kv_heads, BLOCK, head_dim), float("nan"), dtype=td, device="cuda")
+        self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, BLOCK), float("nan"), dtype=td, device="cuda")
+
+    def free(self, blocks):
+        import torch
+        idx = torch.as_tensor(np.asarray(blocks, dtype=np.int64), device="cuda")
+        self.k_pool[idx] = float("nan")
+        self.v_pool[idx] = float("nan")
+
+    def step(self, q, k_rows, v_rows, slots, block_tables, context_lens, cu_q_lens, q_pos, scale, num_heads):
+        import torch
+        from gpu_harness import to_device, to_f64
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        qt = to_device(q, self.dtype)
+        pk.pensieve_kv_append(to_device(k_rows, self.dtype), to_device(v_rows, self.dtype), self.k_pool,
+                              self.v_pool, dev(slots))
+        desc = pk.make_desc(num_heads=num_heads, num_kv_heads=self.k_pool.shape[1], head_dim=self.k_pool.shape[3],
+                            num_blocks=self.num_blocks, block_table_stride=block_tables.shape[1],
+                            dtype={"f32": 0, "f16": 1, "bf16": 2}[self.dtype], softmax_scale=scale,
+                            context_lens_host=context_lens, cu_q_lens_host=cu_q_lens)
+        ws = torch.empty(max(pk.pensieve_attn_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)
+        o = torch.full_like(qt, float("nan"))
+        pk.pensieve_attn_fwd(desc, qt, self.k_pool, self.v_pool, dev(block_tables), dev(context_lens),
+                             dev(cu_q_lens), dev(q_pos), o, ws)
+        torch.cuda.synchronize()
+        return to_f64(o)
+
+
+def run(backend_cls, *, seed, num_convs, steps, num_blocks, num_heads, num_kv_heads, head_dim, dtype, tol,
+        script=None, script_kw=None, stride=None):
+    """Drive ``steps`` serving steps; return SimStats.  Raises AssertionError on a wrong row."""
+    script = conversation_script(seed, num_convs, steps, **(script_kw or {})) if script is None else \
+        np.array(script, dtype=np.int32)
+    steps, num_convs = script.shape
+    totals = script.sum(axis=0).astype(np.int64)
+    # The token values of every conversation, drawn once for its final length.
+    universe = custom_batch(totals, np.zeros_like(totals), num_heads=num_heads, num_kv_heads=num_kv_heads,
+                            head_dim=head_dim, dtype=dtype, seed=seed)
+    kv = [universe.request_kv(c) for c in range(num_convs)]
+    scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+    stride = int(-(-totals.max() // BLOCK)) if stride is None else stride
+
+    backend = backend_cls(num_blocks, num_kv_heads, head_dim, dtype)
+    convs = pk.conversations(np.zeros(num_convs), np.zeros(num_convs), np.zeros(num_convs), np.ones(num_convs))
+    tables = np.full((num_convs, max(stride, 1)), -1, dtype=np.int32)
+    free = list(np.random.default_rng([seed, 5]).permutation(num_blocks).astype(np.int32))
+    last_turn = np.full(num_convs, -1)
+    stats = SimStats()
+    for t in range(steps):
+        convs["activity"] = 1.0 / (1.0 + t - last_turn)
+        while True:
+            convs["new_tokens"] = script[t]
+            try:
+                evict, freed = pk.pensieve_cache_plan_evictions(convs, len(free))
+                break
+            except pk.PensieveError as e:
+                if e.status != pk.PENSIEVE_ERR_UNSUPPORTED or int((script[t] > 0).sum()) <= 1:
+                    raise
+                # Admission is the caller's policy: defer the latest-indexed scheduled
+                # conversation's remaining turns by one step.
+                c = int(np.nonzero(script[t])[0][-1])
+                script[t + 1:, c] = script[t:-1, c].copy()
+                script[t, c] = 0
+                stats.deferred += 1
+        assert freed == int(evict.sum())
+        for c in np.nonzero(evict)[0]:
+            d, e = int(convs["dropped_blocks"][c]), int(evict[c])
+            assert script[t, c] == 0, "a scheduled conversation lost blocks"
+            blocks = tables[c, d:d + e].copy()
+            assert np.all(blocks >= 0)
+            backend.free(blocks)
+            free.extend(int(b) for b in blocks)
+            tables[c, d:d + e] = -1
+            convs["dropped_blocks"][c] = d + e
+            stats.dropped_blocks += e
+            if d + e == -(-int(convs["cached_tokens"][c]) // BLOCK):
+                stats.fully_dropped += 1
+        out = pk.pensieve_cache_build_batch(convs, tables, free)
+        assert out["blocks_used"] <= len(free)
+        del free[:out["blocks_used"]]
+        req_conv, cu, ctx, q_pos = out["request_conv"], out["cu_q_lens"], out["context_lens"], out["q_pos"]
+        T = int(cu[-1])
+        if T:
+            k_rows = np.concatenate([kv[c][0][q_pos[cu[r]:cu[r + 1]]] for r, c in enumerate(req_conv)])
+            v_rows = np.concatenate([kv[c][1][q_pos[cu[r]:cu[r + 1]]] for r, c in enumerate(req_conv)])
+            q = draw_rows((seed, _TAG_STEP_Q, t), (T, num_heads, head_dim), dtype)
+            got = backend.step(q, k_rows, v_rows, out["slot_mapping"], out["req_block_tables"], ctx, cu, q_pos,
+                               scale, num_heads)
+            err = 0.0
+            for r, c in enumerate(req_conv):
+                lo, hi, L = int(cu[r]), int(cu[r + 1]), int(ctx[r])
+                pos = q_pos[lo:hi].astype(np.int64)
+                for h in range(num_heads):
+                    g = oracle.kv_head_of(h, num_heads, num_kv_heads)
+                    ref = oracle.causal_attention(oracle.to_f64(q[lo:hi, h], dtype),
+                                                  oracle.to_f64(kv[c][0][:L, g], dtype),
+                                                  oracle.to_f64(kv[c][1][:L, g], dtype), pos, scale)
+                    e = float(np.max(np.abs(got[lo:hi, h] - ref))) if hi > lo else 0.0
+                    assert np.isfinite(e) and e <= tol, (t, int(c), h, e)
+                    err = max(err, e)
+            stats.max_err = max(stats.max_err, err)
+            stats.rows += T
+            stats.recompute_rows += int(sum(int(convs["dropped_blocks"][c]) and
+                                            min(BLOCK * int(convs["dropped_blocks"][c]),
+                                                int(convs["cached_tokens"][c])) for c in req_conv))
+        stats.per_step.append((t, T, int(evict.sum()), len(free)))
+        sched = script[t] > 0
+        convs["cached_tokens"][sched] += script[t][sched]
+        convs["dropped_blocks"][sched] = 0
+        last_turn[sched] = t
+        stats.steps += 1
+    return stats

@@ -12,6 +12,8 @@ from .batches import (  # noqa: F401
     DTYPE_BYTES,
     bf16_bits_from_f32,
     config_batch,
+    conversation_script,
     custom_batch,
+    draw_rows,
     storage_dtype,
 )

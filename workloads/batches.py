@@ -363,3 +363,37 @@ def config_batch(index: int, *, num_reqs: Optional[int] = None, num_heads: Optio
     num_blocks = 32 if index == 0 else int(math.ceil(1.25 * int(need.sum())))
     bt = _place_blocks(rng, need, num_blocks, int(need.max()))
     return Batch(CONFIG_NAMES[index], dt, hq, hkv, d, B, num_blocks, seed, hist, new, ev, bt)
+
+
+def draw_rows(key, shape, dtype: str, scale: float = 0.5) -> np.ndarray:
+    """Standard normals times ``scale`` of the given shape, from ``default_rng(key)``, in storage dtype."""
+    rng = np.random.default_rng(list(key))
+    x = rng.standard_normal(tuple(shape), dtype=np.float32)
+    x *= np.float32(scale)
+    return _to_storage(x, dtype)
+
+
+def conversation_script(seed: int, num_convs: int, steps: int, *, prompt=(16, 96), answer=(2, 6),
+                        idle=(0, 4)) -> np.ndarray:
+    """new_tokens[step][conversation] of a multi-turn serving run.
+
+    Each conversation alternates idle spells and turns.  A turn is one step
+    that brings the user's prompt (``prompt`` tokens, inclusive range) followed
+    by decode steps of one token each (``answer`` of them); between turns the
+    conversation is idle for ``idle`` steps, so its cache sits unused and may
+    be dropped.  Draws come from ``default_rng((seed, conversation))``.
+    """
+    out = np.zeros((steps, num_convs), dtype=np.int32)
+    for c in range(num_convs):
+        rng = np.random.default_rng([seed, c])
+        t = int(rng.integers(idle[0], idle[1], endpoint=True))
+        while t < steps:
+            out[t, c] = int(rng.integers(prompt[0], prompt[1], endpoint=True))
+            t += 1
+            for _ in range(int(rng.integers(answer[0], answer[1], endpoint=True))):
+                if t >= steps:
+                    break
+                out[t, c] = 1
+                t += 1
+            t += int(rng.integers(idle[0], idle[1], endpoint=True))
+    return out
