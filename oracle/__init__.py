@@ -9,6 +9,12 @@ from .definitions import (  # noqa: F401
     append_kv,
     causal_attention,
     default_positions,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_value,
+    E4M3_MAX,
+    E4M3_VALUES,
+    quantize_e4m3,
     gather_kv,
     kv_head_of,
     causal_visible,

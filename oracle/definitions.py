@@ -45,13 +45,73 @@ import numpy as np
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Decode a storage array (float32, float16, or bfloat16 bit patterns in uint16)."""
+    """Decode a storage array (float32, float16, bfloat16 bit patterns in uint16, E4M3 codes in uint8)."""
     if dtype in ("f32", "f16"):
         return np.asarray(a).astype(np.float64)
     if dtype == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "e4m3":
+        return e4m3_decode(a)
     raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV storage
+# ---------------------------------------------------------------------------
+# The KV cache may be stored as 8-bit floats, halving its memory
+# ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3): KV cache quantised to
+# FP8).  The pages do not fix the format; the reading taken is the OCP 8-bit
+# float E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; an
+# exponent field of 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there
+# are no infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.
+# Each pool carries one float32 scale: stored code = E4M3(x / scale), value
+# read back = decoded code * scale.
+
+def e4m3_value(code: int) -> float:
+    """Value of one E4M3 code, from the bit fields."""
+    sign = -1.0 if code & 0x80 else 1.0
+    exp_field = (code >> 3) & 0xF
+    mant = code & 0x7
+    if exp_field == 0xF and mant == 0x7:
+        return float("nan")
+    if exp_field == 0:
+        return sign * (mant / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + mant / 8.0) * 2.0 ** (exp_field - 7)
+
+
+E4M3_VALUES = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (float64) of an array of E4M3 codes."""
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each value, ties to the even code; beyond +-448 saturates; NaN -> 0x7F.
+
+    The sign bit follows the sign of the input (so -0.0 and small negatives that
+    round to zero give 0x80).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.minimum(np.abs(x), E4M3_MAX)
+    grid = E4M3_VALUES[:0x7F]                     # codes 0 .. 0x7E, ascending magnitudes
+    hi = np.clip(np.searchsorted(grid, mag, side="left"), 0, len(grid) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - grid[lo]
+    d_hi = grid[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_e4m3(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
+    """Storage codes of values x (storage dtype ``dtype``): E4M3 of x / scale, the division in float32."""
+    xf = to_f64(x, dtype).astype(np.float32)
+    return e4m3_encode(xf / np.float32(scale))
 
 
 # ---------------------------------------------------------------------------
@@ -76,8 +136,11 @@ def append_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: 
 # Attention
 # ---------------------------------------------------------------------------
 def gather_kv(k_pool, v_pool, block_table_row, context_len: int, kv_head: int, block_size: int,
-              dtype: str):
-    """Follow a block table: return this request's K and V as contiguous [L][d] float64 arrays."""
+              dtype: str, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Follow a block table: return this request's K and V as contiguous [L][d] float64 arrays.
+
+    Decoded pool values are multiplied by the pool's scale (1 for float pools).
+    """
     n_blocks = -(-context_len // block_size)
     k_rows, v_rows = [], []
     for j in range(n_blocks):
@@ -87,8 +150,8 @@ def gather_kv(k_pool, v_pool, block_table_row, context_len: int, kv_head: int, b
     d = k_pool.shape[-1]
     if n_blocks == 0:
         return np.zeros((0, d)), np.zeros((0, d))
-    k = np.concatenate(k_rows, axis=0)[:context_len]
-    v = np.concatenate(v_rows, axis=0)[:context_len]
+    k = np.concatenate(k_rows, axis=0)[:context_len] * float(k_scale)
+    v = np.concatenate(v_rows, axis=0)[:context_len] * float(v_scale)
     return k, v
 
 
@@ -137,8 +200,14 @@ def row_positions(q_pos: Optional[np.ndarray], lo: int, hi: int, context_len: in
 def paged_attention(q: np.ndarray, k_pool, v_pool, block_tables: np.ndarray,
                     context_lens: np.ndarray, cu_q_lens: np.ndarray, q_pos: Optional[np.ndarray],
                     softmax_scale: float, dtype: str, *, requests: Optional[Iterable[int]] = None,
-                    heads: Optional[Iterable[int]] = None) -> np.ndarray:
-    """O [T][Hq][d] float64 for the unified batch (rows of skipped requests/heads are NaN)."""
+                    heads: Optional[Iterable[int]] = None, kv_dtype: Optional[str] = None,
+                    k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """O [T][Hq][d] float64 for the unified batch (rows of skipped requests/heads are NaN).
+
+    ``dtype`` is the storage type of Q; the pools hold ``kv_dtype`` (default: the
+    same), read back as decoded value times k_scale / v_scale.
+    """
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     T, Hq, d = q.shape
     Hkv = k_pool.shape[1]
     block_size = k_pool.shape[2]
@@ -151,7 +220,7 @@ def paged_attention(q: np.ndarray, k_pool, v_pool, block_tables: np.ndarray,
         pos = row_positions(q_pos, lo, hi, L)
         for h in head_list:
             g = kv_head_of(h, Hq, Hkv)
-            k, v = gather_kv(k_pool, v_pool, block_tables[r], L, g, block_size, dtype)
+            k, v = gather_kv(k_pool, v_pool, block_tables[r], L, g, block_size, kv_dtype, k_scale, v_scale)
             out[lo:hi, h, :] = causal_attention(to_f64(q[lo:hi, h, :], dtype), k, v, pos, softmax_scale)
     return out
 
@@ -197,8 +266,10 @@ def partial_attention(q_rows, k, v, positions, scale, start: int, end: int):
 
 def split_partial(q: np.ndarray, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos,
                   softmax_scale: float, dtype: str, num_partitions: int, *,
-                  requests: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None):
+                  requests: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None,
+                  kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Partials part_o [T][Hq][P][d], part_m [T][Hq][P], part_l [T][Hq][P] (float64)."""
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     T, Hq, d = q.shape
     Hkv = k_pool.shape[1]
     block_size = k_pool.shape[2]
@@ -215,7 +286,7 @@ def split_partial(q: np.ndarray, k_pool, v_pool, block_tables, context_lens, cu_
         ranges = partition_token_ranges(L, P, block_size)
         for h in head_list:
             g = kv_head_of(h, Hq, Hkv)
-            k, v = gather_kv(k_pool, v_pool, block_tables[r], L, g, block_size, dtype)
+            k, v = gather_kv(k_pool, v_pool, block_tables[r], L, g, block_size, kv_dtype, k_scale, v_scale)
             qr = to_f64(q[lo:hi, h, :], dtype)
             for p_idx, (s, e) in enumerate(ranges):
                 o, m, l = partial_attention(qr, k, v, pos, softmax_scale, s, e)
@@ -251,7 +322,7 @@ def visible_pairs(context_lens, cu_q_lens, q_pos) -> int:
 
 
 __all__ = [
-    "to_f64", "append_kv", "gather_kv", "kv_head_of", "causal_visible", "causal_attention",
+    "to_f64", "e4m3_value", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "E4M3_VALUES", "E4M3_MAX", "append_kv", "gather_kv", "kv_head_of", "causal_visible", "causal_attention",
     "default_positions", "row_positions", "paged_attention",
     "partition_token_ranges", "partial_attention", "split_partial", "split_merge", "visible_pairs",
 ]
