@@ -68,19 +68,26 @@ class DeviceBatch:
     through them, so a step's K/V and Q cannot still sit in the 256 MB last-level cache
     (MALL) from the step before (the working set of two copies exceeds it on every workload)."""
 
-    def __init__(self, batch, copies: int = 2):
+    def __init__(self, batch, copies: int = 2, kv_fp8=None):
         import torch
         self.b = b = batch
         td = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[b.dtype]
         self.td = td
-        self.k_pool = torch.empty((b.num_blocks, b.num_kv_heads, 16, b.head_dim), dtype=td, device="cuda")
-        self.v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.head_dim, 16), dtype=td, device="cuda")
-        self.k_pool.fill_(float("nan"))
-        self.v_pool.fill_(float("nan"))
+        self.kv_fp8 = kv_fp8                      # (k_scale, v_scale): E4M3 pools
+        self.kv_bytes = 1 if kv_fp8 else b.elem_bytes
+        pd = torch.uint8 if kv_fp8 else td
+        self.k_pool = torch.empty((b.num_blocks, b.num_kv_heads, 16, b.head_dim), dtype=pd, device="cuda")
+        self.v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.head_dim, 16), dtype=pd, device="cuda")
+        if kv_fp8:
+            self.k_pool.fill_(0x7F)
+            self.v_pool.fill_(0x7F)
+        else:
+            self.k_pool.fill_(float("nan"))
+            self.v_pool.fill_(float("nan"))
         for r, k, v, slots, pos in b.iter_requests():
             if len(pos):
-                pk.pensieve_kv_append(self._dev(k[pos]), self._dev(v[pos]), self.k_pool, self.v_pool,
-                                      torch.from_numpy(slots.copy()).cuda())
+                self._append(self._dev(k[pos]), self._dev(v[pos]), self.k_pool, self.v_pool,
+                             torch.from_numpy(slots.copy()).cuda())
         kn, vn = b.new_kv()
         self.k_new, self.v_new = self._dev(kn), self._dev(vn)
         self.new_slots = torch.from_numpy(b.new_slots.copy()).cuda()
@@ -90,10 +97,11 @@ class DeviceBatch:
         self.ctx = torch.from_numpy(b.context_lens.copy()).cuda()
         self.cu = torch.from_numpy(b.cu_q_lens.copy()).cuda()
         self.q_pos = None if b.has_default_positions else torch.from_numpy(b.q_pos.copy()).cuda()
+        fp8 = {} if not kv_fp8 else dict(kv_dtype=pk.PENSIEVE_FP8_E4M3, k_scale=kv_fp8[0], v_scale=kv_fp8[1])
         self.desc = pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                                  num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
                                  dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
-                                 context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens)
+                                 context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens, **fp8)
         self.ws = torch.empty(max(pk.pensieve_attn_workspace_size(self.desc), 256), dtype=torch.uint8, device="cuda")
         self.sets = [(self.k_pool, self.v_pool, self.q, self.o)]
         for _ in range(copies - 1):
@@ -106,6 +114,12 @@ class DeviceBatch:
         self.turn += 1
         return s
 
+    def _append(self, k, v, k_pool, v_pool, slots):
+        if self.kv_fp8:
+            pk.pensieve_kv_append_fp8(k, v, k_pool, v_pool, slots, self.kv_fp8[0], self.kv_fp8[1])
+        else:
+            pk.pensieve_kv_append(k, v, k_pool, v_pool, slots)
+
     def _dev(self, arr):
         import torch
         if self.b.dtype == "bf16":
@@ -115,7 +129,7 @@ class DeviceBatch:
     def step(self):
         """The whole path: append the step's new rows, then attention over the batch."""
         k_pool, v_pool, q, o = self._next()
-        pk.pensieve_kv_append(self.k_new, self.v_new, k_pool, v_pool, self.new_slots)
+        self._append(self.k_new, self.v_new, k_pool, v_pool, self.new_slots)
         pk.pensieve_attn_fwd(self.desc, q, k_pool, v_pool, self.bt, self.ctx, self.cu, self.q_pos, o, self.ws)
 
     def attn(self):
@@ -143,13 +157,15 @@ class DeviceBatch:
 # ---------------------------------------------------------------------------
 # algorithmic work
 # ---------------------------------------------------------------------------
-def request_bytes(b, r: int) -> int:
-    """Bytes the method must move for request r: its K and V once per KV head,
-    its Q rows in and O rows out, its block-table entries, lengths and positions."""
+def request_bytes(b, r: int, kv_bytes=None) -> int:
+    """Bytes the method must move for request r: its K and V once per KV head (kv_bytes per
+    element: the pools' type), its Q rows in and O rows out, its block-table entries, lengths
+    and positions."""
     e = b.elem_bytes
+    kb = e if kv_bytes is None else kv_bytes
     L, q = int(b.context_lens[r]), int(b.q_lens[r])
     nblk = -(-L // 16)
-    kv = 2 * L * b.num_kv_heads * b.head_dim * e
+    kv = 2 * L * b.num_kv_heads * b.head_dim * kb
     qo = 2 * q * b.num_heads * b.head_dim * e
     meta = 4 * nblk + 8 + (0 if b.has_default_positions else 4 * q)
     return kv + qo + meta
@@ -183,15 +199,16 @@ def kernel_work(dev: DeviceBatch, kernel: str):
         k0, k1 = int(part) * per, min((int(part) + 1) * per, L)
         seen = np.clip(np.minimum(pos + 1, k1) - k0, 0, None)
         flops += 4 * b.head_dim * int(hc) * int(seen.sum())
-    nbytes += sum(2 * k * b.head_dim * e for k in keys.values())
+    nbytes += sum(2 * k * b.head_dim * dev.kv_bytes for k in keys.values())
     for r in reqs:
         nbytes += 4 * (-(-int(b.context_lens[r]) // 16)) + 8 + (0 if b.has_default_positions else 4 * int(b.q_lens[r]))
     return nbytes, flops
 
 
-def append_bytes(b) -> int:
+def append_bytes(b, kv_bytes=None) -> int:
     """Read K/V new rows and write them into the pools (+ slot ids)."""
-    return 2 * 2 * b.total_q * b.num_kv_heads * b.head_dim * b.elem_bytes + 4 * b.total_q
+    kb = b.elem_bytes if kv_bytes is None else kv_bytes
+    return 2 * b.total_q * b.num_kv_heads * b.head_dim * (b.elem_bytes + kb) + 4 * b.total_q
 
 
 # ---------------------------------------------------------------------------
@@ -238,7 +255,7 @@ def roofline_for(b, dev, per, kernel: str, counters):
     if kernel in PLAN_KERNELS.values():
         nbytes, flops = kernel_work(dev, kernel)
     elif kernel == "kv_append":
-        nbytes, flops = append_bytes(b), 0
+        nbytes, flops = append_bytes(b, dev.kv_bytes), 0
     else:
         nbytes, flops = 0, 0
     avg_s = per[kernel]["avg_ms"] * 1e-3
@@ -246,7 +263,7 @@ def roofline_for(b, dev, per, kernel: str, counters):
     ridge = MFMA_PEAK_TFLOPS[b.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = None
     if counters:
-        c = counters.get(f"{kernel}@{b.name}")
+        c = counters.get(f"{kernel}@{b.name}") if dev.kv_fp8 is None else None
         if c and c.get("source_sha") == source_digest(kernel):
             traffic = c.get("traffic_bytes_per_launch")
     if intensity < ridge:
@@ -419,6 +436,32 @@ def secondary(index: int, steps: int, warmup: int, counters):
     return out
 
 
+FP8_SCALES = (1 / 128, 1 / 128)   # the workloads' K/V (0.5 N(0,1)) stay below 3, i.e. codes below 384
+
+
+def fp8_measure(index: int, steps: int, warmup: int, full_step: bool):
+    """The same workload with E4M3 pools: whole step (append + attention) or attention alone."""
+    import torch
+    b = config_batch(index)
+    dev = DeviceBatch(b, kv_fp8=FP8_SCALES)
+    ms, trace = time_steps(dev.step if full_step else dev.attn, steps, warmup)
+    per = summarize_trace(trace, steps)
+    attn = {k: v for k, v in per.items() if k.startswith("attn")}
+    dom = max(attn, key=lambda k: attn[k]["total_ms"])
+    out = {"workload": b.name, "kv_dtype": "fp8_e4m3", "scales": list(FP8_SCALES),
+           "timed": "step (append + attention)" if full_step else "attention",
+           "ms": round(ms, 4), "query_tokens_per_s": round(b.total_q / (ms * 1e-3), 1),
+           "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per.items()},
+           "roofline": roofline_for(b, dev, per, dom, None)}
+    attn_ms = sum(v["per_step_ms"] for v in attn.values())
+    total_bytes = sum(request_bytes(b, r, 1) for r in range(b.num_reqs))
+    out["attn_total"] = {"ms": round(attn_ms, 4), "bytes": total_bytes,
+                         "hbm_frac": round(total_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -489,6 +532,12 @@ def main():
         for idx in (2, 3, 4):
             log(f"secondary workload {idx}")
             result["secondary"].append(secondary(idx, max(20, args.steps // 4), 5, counters))
+    if not args.no_secondary:
+        result["fp8_kv"] = []
+        for idx in (1, 2, 3):
+            log(f"fp8 KV pools, workload {idx}")
+            result["fp8_kv"].append(fp8_measure(idx, max(20, args.steps // 4) if idx != 1 else args.steps,
+                                                5 if idx != 1 else args.warmup, full_step=idx == 1))
     if not args.no_cpu:
         log("cpu_baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)

@@ -24,10 +24,14 @@
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *   device work is enqueued on it asynchronously; a call returns before the
  *   GPU finishes.  Host arrays (_host) are fully read before the call returns.
- * - Element type of Q, O and both pools: pensieve_dtype (F32, F16, BF16).
+ * - Element type of Q, O and both pools: pensieve_dtype (F32, F16, BF16);
+ *   with F16/BF16 queries the pools may instead hold FP8_E4M3 codes
+ *   (desc.kv_dtype, with a scale per pool).
  *   Arithmetic: dot products, softmax and accumulation in fp32; on F16/BF16
  *   the softmax weights are rounded to the input type before the P.V product;
- *   outputs are rounded to nearest-even.
+ *   outputs are rounded to nearest-even.  E4M3 codes are widened exactly
+ *   (every E4M3 value is an F16 and a BF16 value); the K scale is folded into
+ *   the softmax scale and the V scale into the output normalisation.
  * - block_size must be 16; head_dim must be 64 or 128; num_heads must be a
  *   multiple of num_kv_heads.  Query head h reads KV head
  *   h / (num_heads / num_kv_heads).
@@ -72,7 +76,17 @@ typedef enum pensieve_status {
   PENSIEVE_ERR_HIP = 4
 } pensieve_status;
 
-typedef enum pensieve_dtype { PENSIEVE_F32 = 0, PENSIEVE_F16 = 1, PENSIEVE_BF16 = 2 } pensieve_dtype;
+/* PENSIEVE_FP8_E4M3: pool storage only -- OCP 8-bit floats E4M3 (sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN,
+ * largest finite 448), each pool with one float32 scale: the value read back is
+ * the decoded code times the pool's scale ("LLM上下文缓存与状态复用机制的分析和探索",
+ * section 4(3): the KV cache stored in FP8 to halve its memory). */
+typedef enum pensieve_dtype {
+  PENSIEVE_F32 = 0,
+  PENSIEVE_F16 = 1,
+  PENSIEVE_BF16 = 2,
+  PENSIEVE_FP8_E4M3 = 3
+} pensieve_dtype;
 
 /* pensieve_batch_desc.flags: route every work item to the vector-ALU kernel
  * (the matrix-core kernel is otherwise used for items with many query rows
@@ -90,11 +104,15 @@ typedef struct pensieve_batch_desc {
   int32_t block_size;           /* 16 */
   int32_t num_blocks;           /* blocks in each pool */
   int32_t block_table_stride;   /* int32 entries per block-table row */
-  int32_t dtype;                /* pensieve_dtype */
+  int32_t dtype;                /* pensieve_dtype of Q and O (F32, F16, BF16) */
   float softmax_scale;          /* scale on q.k before the softmax, e.g. 1/sqrt(head_dim); > 0 */
   int32_t flags;                /* 0, or PENSIEVE_FLAG_VECTOR_ONLY */
   const int32_t* context_lens_host;  /* [num_reqs] */
   const int32_t* cu_q_lens_host;     /* [num_reqs + 1], cu_q_lens_host[0] == 0 */
+  int32_t kv_dtype;             /* element type of both pools: dtype itself, or
+                                   PENSIEVE_FP8_E4M3 when dtype is F16 or BF16 */
+  float k_scale, v_scale;       /* FP8_E4M3 pools: value = code * scale (finite, > 0);
+                                   ignored for other pools */
 } pensieve_batch_desc;
 
 /* Library version string, e.g. "pensieve 0.1 gfx950". */
@@ -118,6 +136,22 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
                                    const int32_t* slot_mapping, int32_t num_tokens,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int32_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * KV append into FP8_E4M3 pools: as pensieve_kv_append, but k_new / v_new hold
+ * src_dtype (F16 or BF16) values and each pool element receives the E4M3 code
+ * of value / scale (k_scale for K, v_scale for V): the quotient is computed in
+ * float32 with correct rounding, magnitudes beyond 448 saturate to +-448, and
+ * the rest round to the nearest code, ties to even; NaN stays NaN.  The pools
+ * are [num_blocks][Hkv][16][d] and [num_blocks][Hkv][d][16] bytes.  Scales
+ * must be finite and > 0 (INVALID_ARG otherwise).  Reading: the pages name
+ * FP8 KV storage without a format or a scaling rule; OCP E4M3 with one scale
+ * per pool is taken ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3)).
+ */
+pensieve_status pensieve_kv_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                       const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t src_dtype,
+                                       float k_scale, float v_scale, void* stream);
 
 /*
  * Block swap with a host tier ("Stateful Large Language Model Serving with

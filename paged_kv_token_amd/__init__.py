@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     PENSIEVE_ERR_UNSUPPORTED,
     PENSIEVE_F16,
     PENSIEVE_F32,
+    PENSIEVE_FP8_E4M3,
     PENSIEVE_FLAG_VECTOR_ONLY,
     dtype_code,
     load_library,
@@ -27,6 +28,7 @@ from .binding import (  # noqa: F401
     pensieve_cache_plan_evictions,
     pensieve_debug_plan,
     pensieve_kv_append,
+    pensieve_kv_append_fp8,
     pensieve_kv_swap_in,
     pensieve_kv_swap_out,
     pensieve_trace_enable,

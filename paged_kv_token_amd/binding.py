@@ -23,14 +23,14 @@ PENSIEVE_ERR_INVALID_ARG = 1
 PENSIEVE_ERR_UNSUPPORTED = 2
 PENSIEVE_ERR_WORKSPACE_TOO_SMALL = 3
 PENSIEVE_ERR_HIP = 4
-PENSIEVE_F32, PENSIEVE_F16, PENSIEVE_BF16 = 0, 1, 2
+PENSIEVE_F32, PENSIEVE_F16, PENSIEVE_BF16, PENSIEVE_FP8_E4M3 = 0, 1, 2, 3
 PENSIEVE_FLAG_VECTOR_ONLY = 1
 
 EXPORTED = (
     "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",
     "pensieve_attn_fwd", "pensieve_attn_split_partial", "pensieve_attn_split_merge", "pensieve_debug_plan",
     "pensieve_trace_enable", "pensieve_trace_read", "pensieve_kv_swap_out", "pensieve_kv_swap_in",
-    "pensieve_cache_plan_evictions", "pensieve_cache_build_batch",
+    "pensieve_cache_plan_evictions", "pensieve_cache_build_batch", "pensieve_kv_append_fp8",
 )
 TRACE_KERNELS = {0: "kv_append", 1: "attn_vector", 2: "attn_mfma", 3: "split_merge", 4: "kv_swap"}
 
@@ -57,6 +57,9 @@ class BatchDesc(ctypes.Structure):
         ("flags", ctypes.c_int32),
         ("context_lens_host", ctypes.POINTER(ctypes.c_int32)),
         ("cu_q_lens_host", ctypes.POINTER(ctypes.c_int32)),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -85,6 +88,8 @@ def load_library(path: Optional[str] = None):
     lib.pensieve_version.restype = ctypes.c_char_p
     lib.pensieve_last_error.restype = ctypes.c_char_p
     lib.pensieve_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    f32 = ctypes.c_float
+    lib.pensieve_kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.pensieve_kv_swap_out.argtypes = [vp, vp, i32, vp, vp, i32, i32p, i32p, i32, i32, i32, i32, vp]
     lib.pensieve_kv_swap_in.argtypes = [vp, vp, i32, vp, vp, i32, i32p, i32p, i32, i32, i32, i32, vp]
     lib.pensieve_attn_workspace_size.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
@@ -117,8 +122,19 @@ def _torch():
 
 
 def dtype_code(t) -> int:
+    """pensieve_dtype of a tensor; uint8 and float8_e4m3fn tensors are E4M3 pools."""
     torch = _torch()
-    return {torch.float32: PENSIEVE_F32, torch.float16: PENSIEVE_F16, torch.bfloat16: PENSIEVE_BF16}[t.dtype]
+    return {torch.float32: PENSIEVE_F32, torch.float16: PENSIEVE_F16, torch.bfloat16: PENSIEVE_BF16,
+            torch.uint8: PENSIEVE_FP8_E4M3, torch.float8_e4m3fn: PENSIEVE_FP8_E4M3}[t.dtype]
+
+
+def _pool_ptr(t, name: str, desc_or_code, q=None):
+    """A pool tensor: the query dtype, or (E4M3 pools) uint8 / float8_e4m3fn."""
+    code = desc_or_code.kv_dtype if isinstance(desc_or_code, BatchDesc) else int(desc_or_code)
+    p = _ptr(t, name)
+    if p is not None and dtype_code(t) != code:
+        raise ValueError(f"{name} holds {t.dtype}, which does not match kv_dtype {code}")
+    return p
 
 
 def _ptr(t, name: str, dtype=None):
@@ -144,13 +160,17 @@ def _stream(stream):
 
 def make_desc(*, num_heads: int, num_kv_heads: int, head_dim: int, num_blocks: int, block_table_stride: int,
               dtype: int, softmax_scale: float, context_lens_host, cu_q_lens_host, block_size: int = 16,
-              flags: int = 0) -> BatchDesc:
+              flags: int = 0, kv_dtype: Optional[int] = None, k_scale: float = 1.0,
+              v_scale: float = 1.0) -> BatchDesc:
     ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
     cu = np.ascontiguousarray(cu_q_lens_host, dtype=np.int32)
     d = BatchDesc(len(ctx), num_heads, num_kv_heads, head_dim, block_size, num_blocks, block_table_stride, dtype,
                   float(softmax_scale), flags,
                   ctx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                   cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    d.kv_dtype = dtype if kv_dtype is None else int(kv_dtype)
+    d.k_scale = float(k_scale)
+    d.v_scale = float(v_scale)
     d._keep = (ctx, cu)  # host arrays must outlive the descriptor
     return d
 
@@ -169,6 +189,20 @@ def pensieve_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None):
                                   _ptr(k_pool, "k_pool", k_new.dtype), _ptr(v_pool, "v_pool", k_new.dtype),
                                   _ptr(slot_mapping, "slot_mapping", torch.int32), n, hkv, d, k_pool.shape[2], nb,
                                   dtype_code(k_new), _stream(stream)))
+
+
+def pensieve_kv_append_fp8(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale: float, v_scale: float,
+                           stream=None):
+    """Append f16 / bf16 rows into E4M3 pools (uint8 or float8_e4m3fn tensors): code = E4M3(x / scale)."""
+    torch = _torch()
+    lib = load_library()
+    n, hkv, d = k_new.shape
+    nb = k_pool.shape[0]
+    _check(lib.pensieve_kv_append_fp8(_ptr(k_new, "k_new"), _ptr(v_new, "v_new", k_new.dtype),
+                                      _pool_ptr(k_pool, "k_pool", PENSIEVE_FP8_E4M3),
+                                      _pool_ptr(v_pool, "v_pool", PENSIEVE_FP8_E4M3),
+                                      _ptr(slot_mapping, "slot_mapping", torch.int32), n, hkv, d, k_pool.shape[2], nb,
+                                      dtype_code(k_new), float(k_scale), float(v_scale), _stream(stream)))
 
 
 def _host_ptr(t, name: str, dtype):
@@ -217,7 +251,7 @@ def pensieve_attn_fwd(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_
                       workspace, stream=None):
     torch = _torch()
     _check(load_library().pensieve_attn_fwd(
-        ctypes.byref(desc), _ptr(q, "q"), _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
+        ctypes.byref(desc), _ptr(q, "q"), _pool_ptr(k_pool, "k_pool", desc), _pool_ptr(v_pool, "v_pool", desc),
         _ptr(block_tables, "block_tables", torch.int32), _ptr(context_lens, "context_lens", torch.int32),
         _ptr(cu_q_lens, "cu_q_lens", torch.int32), _ptr(q_pos, "q_pos", torch.int32), _ptr(o, "o", q.dtype),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
@@ -228,8 +262,8 @@ def pensieve_attn_split_partial(desc: BatchDesc, num_partitions: int, q, k_pool,
                                 context_lens, cu_q_lens, q_pos, part_o, part_m, part_l, workspace, stream=None):
     torch = _torch()
     _check(load_library().pensieve_attn_split_partial(
-        ctypes.byref(desc), num_partitions, _ptr(q, "q"), _ptr(k_pool, "k_pool", q.dtype),
-        _ptr(v_pool, "v_pool", q.dtype), _ptr(block_tables, "block_tables", torch.int32),
+        ctypes.byref(desc), num_partitions, _ptr(q, "q"), _pool_ptr(k_pool, "k_pool", desc),
+        _pool_ptr(v_pool, "v_pool", desc), _ptr(block_tables, "block_tables", torch.int32),
         _ptr(context_lens, "context_lens", torch.int32), _ptr(cu_q_lens, "cu_q_lens", torch.int32),
         _ptr(q_pos, "q_pos", torch.int32), _ptr(part_o, "part_o", torch.float32),
         _ptr(part_m, "part_m", torch.float32), _ptr(part_l, "part_l", torch.float32),

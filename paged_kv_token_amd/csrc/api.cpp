@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -68,9 +69,13 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int elem_bytes(int dtype) { return dtype == PENSIEVE_F32 ? 4 : 2; }
+int elem_bytes(int dtype) { return dtype == PENSIEVE_F32 ? 4 : dtype == PENSIEVE_FP8_E4M3 ? 1 : 2; }
 
+// Types of Q / O (and of pools that hold the query type).
 bool valid_dtype(int dtype) { return dtype == PENSIEVE_F32 || dtype == PENSIEVE_F16 || dtype == PENSIEVE_BF16; }
+// Types a pool may hold.
+bool valid_pool_dtype(int dtype) { return valid_dtype(dtype) || dtype == PENSIEVE_FP8_E4M3; }
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 int next_pow2(int x) {
   int p = 1;
@@ -90,6 +95,14 @@ pensieve_status check_desc(const pensieve_batch_desc* d) {
     return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d->head_dim);
   if (d->block_size != kBlockSize) return fail(PENSIEVE_ERR_UNSUPPORTED, "block_size %d unsupported (16)", d->block_size);
   if (!valid_dtype(d->dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+  if (d->kv_dtype != d->dtype) {
+    if (d->kv_dtype != PENSIEVE_FP8_E4M3)
+      return fail(PENSIEVE_ERR_UNSUPPORTED, "kv_dtype %d with dtype %d: pools hold dtype or FP8_E4M3", d->kv_dtype,
+                  d->dtype);
+    if (d->dtype == PENSIEVE_F32) return fail(PENSIEVE_ERR_UNSUPPORTED, "FP8_E4M3 pools need F16 or BF16 queries");
+    if (!valid_scale(d->k_scale) || !valid_scale(d->v_scale))
+      return fail(PENSIEVE_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  }
   if (d->num_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_blocks must be > 0");
   if (d->block_table_stride <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "block_table_stride must be > 0");
   if (!(d->softmax_scale > 0.f)) return fail(PENSIEVE_ERR_INVALID_ARG, "softmax_scale must be > 0");
@@ -345,16 +358,22 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
 // An event per buffer guards its reuse until the copy has finished.
 struct Stager {
   static constexpr int kSlots = 32;   // deep enough that a long swap does not hold up later calls
+  // Every slot starts as a slice of one page-locked slab, so that the first pass over the ring
+  // allocates nothing (a page-locked free synchronises the device); only a work list longer
+  // than a slice gives its slot a buffer of its own.
+  static constexpr size_t kSlotBytes = 512 * 1024;
   struct Slot {
     void* host = nullptr;
     void* mapped = nullptr;   // the same buffer as seen from the device
     size_t cap = 0;
+    bool owned = false;       // a buffer of its own (else a slice of the slab)
     hipEvent_t ev = nullptr;
     bool pending = false;
   };
   std::mutex mu;
   Slot slots[kSlots];
   int next = 0;
+  void* slab = nullptr;
 };
 
 std::mutex g_stagers_mu;
@@ -380,6 +399,17 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
   std::lock_guard<std::mutex> lk(st->mu);
+  if (!st->slab) {
+    if ((e = hipHostMalloc(&st->slab, Stager::kSlots * Stager::kSlotBytes, hipHostMallocMapped)) != hipSuccess)
+      return e;
+    void* slab_mapped = nullptr;
+    if ((e = hipHostGetDevicePointer(&slab_mapped, st->slab, 0)) != hipSuccess) return e;
+    for (int i = 0; i < Stager::kSlots; ++i) {
+      st->slots[i].host = static_cast<uint8_t*>(st->slab) + i * Stager::kSlotBytes;
+      st->slots[i].mapped = static_cast<uint8_t*>(slab_mapped) + i * Stager::kSlotBytes;
+      st->slots[i].cap = Stager::kSlotBytes;
+    }
+  }
   Stager::Slot& s = st->slots[st->next];
   st->next = (st->next + 1) % Stager::kSlots;
   if (s.pending) {
@@ -387,12 +417,15 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
     s.pending = false;
   }
   if (s.cap < bytes) {
-    if (s.host && (e = hipHostFree(s.host)) != hipSuccess) return e;
+    if (s.owned && (e = hipHostFree(s.host)) != hipSuccess) return e;
     s.host = nullptr;
-    size_t cap = std::max<size_t>(bytes, 64 * 1024);
+    s.owned = false;
+    size_t cap = 2 * Stager::kSlotBytes;
+    while (cap < bytes) cap *= 2;
     if ((e = hipHostMalloc(&s.host, cap, hipHostMallocMapped)) != hipSuccess) return e;
     if ((e = hipHostGetDevicePointer(&s.mapped, s.host, 0)) != hipSuccess) return e;
     s.cap = cap;
+    s.owned = true;
   }
   if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
   std::memcpy(s.host, src, bytes);
@@ -589,9 +622,9 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     const hipStream_t st = (fork && s.kernel == kVector) ? conc->side : stream;
     TraceScope trace(s.kernel == kMatrix ? kTraceMatrix : kTraceVector, s.count, st);
     if (s.kernel == kMatrix)
-      e = pk::launch_attn_mfma(a, d->dtype, d->head_dim, s.param, st);
+      e = pk::launch_attn_mfma(a, d->dtype, d->kv_dtype, d->head_dim, s.param, st);
     else
-      e = pk::launch_attn_vector(a, d->dtype, d->head_dim, s.param, st);
+      e = pk::launch_attn_vector(a, d->dtype, d->kv_dtype, d->head_dim, s.param, st);
     if (e != hipSuccess) return hip_fail(e, s.kernel == kMatrix ? "matrix-core attention launch" : "vector attention launch");
   }
   if (fork) {
@@ -621,8 +654,12 @@ pk::AttnArgs make_args(const pensieve_batch_desc* d, const void* q, const void* 
   a.num_heads = d->num_heads;
   a.num_kv_heads = d->num_kv_heads;
   a.bt_stride = d->block_table_stride;
-  a.scale = d->softmax_scale;
-  a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  // E4M3 pools: the kernels take q.k over the stored codes, so the K scale joins the softmax
+  // scale, and the V scale multiplies the normalised output.
+  const bool f8 = d->kv_dtype == PENSIEVE_FP8_E4M3;
+  a.scale = d->softmax_scale * (f8 ? d->k_scale : 1.f);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.v_scale = f8 ? d->v_scale : 1.f;
   return a;
 }
 
@@ -653,7 +690,7 @@ pensieve_status kv_swap(bool to_host, void* k_pool, void* v_pool, int32_t num_bl
   if (n < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "n < 0");
   if (num_kv_heads <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_kv_heads must be > 0");
   if (head_dim != 64 && head_dim != 128) return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported", head_dim);
-  if (!valid_dtype(dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!valid_pool_dtype(dtype)) return fail(PENSIEVE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (num_blocks <= 0 || num_host_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "pool sizes must be > 0");
   if (n == 0) return ok();
   if (!k_pool || !v_pool || !k_host || !v_host) return fail(PENSIEVE_ERR_INVALID_ARG, "a pool pointer is NULL");
@@ -744,6 +781,30 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
   hipError_t e = pk::launch_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
                                       elem_bytes(dtype), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return ok();
+}
+
+pensieve_status pensieve_kv_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                       const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t src_dtype,
+                                       float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_kv_heads <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+  if (head_dim != 64 && head_dim != 128) return fail(PENSIEVE_ERR_UNSUPPORTED, "head_dim %d unsupported", head_dim);
+  if (block_size != kBlockSize) return fail(PENSIEVE_ERR_UNSUPPORTED, "block_size %d unsupported", block_size);
+  if (src_dtype != PENSIEVE_F16 && src_dtype != PENSIEVE_BF16)
+    return fail(PENSIEVE_ERR_UNSUPPORTED, "src_dtype %d unsupported (F16 or BF16)", src_dtype);
+  if (!valid_scale(k_scale) || !valid_scale(v_scale))
+    return fail(PENSIEVE_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  if (num_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_blocks must be > 0");
+  if (num_kv_heads > 65535) return fail(PENSIEVE_ERR_UNSUPPORTED, "num_kv_heads > 65535");
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
+    return fail(PENSIEVE_ERR_INVALID_ARG, "a device pointer is NULL");
+  TraceScope trace(kTraceAppend, num_tokens, static_cast<hipStream_t>(stream));
+  hipError_t e = pk::launch_kv_append_fp8(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads,
+                                          head_dim, src_dtype, k_scale, v_scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_append_fp8 launch");
   return ok();
 }
 

@@ -38,6 +38,18 @@ struct Mfma;
 template <>
 struct Mfma<kF16> {
   typedef _Float16 vec8 __attribute__((ext_vector_type(8)));
+  // Eight E4M3 codes (bytes of w in order) as f16 values, exactly (two per conversion).
+  static __device__ __forceinline__ vec8 from_e4m3(u32x2 w) {
+    vec8 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t word = w[i];
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true);
+      r[4 * i] = lo[0]; r[4 * i + 1] = lo[1]; r[4 * i + 2] = hi[0]; r[4 * i + 3] = hi[1];
+    }
+    return r;
+  }
   static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -52,6 +64,17 @@ struct Mfma<kF16> {
 template <>
 struct Mfma<kBF16> {
   typedef __bf16 vec8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ vec8 from_e4m3(u32x2 w) {
+    vec8 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t word = w[i];
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true);
+      r[4 * i] = lo[0]; r[4 * i + 1] = lo[1]; r[4 * i + 2] = hi[0]; r[4 * i + 3] = hi[1];
+    }
+    return r;
+  }
   static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -81,6 +104,19 @@ __device__ __forceinline__ u32x4 zero_keys_from(u32x4 v, int first, int limit) {
     uint32_t keep = 0;
     if (first + 2 * wd < limit) keep |= 0x0000FFFFu;
     if (first + 2 * wd + 1 < limit) keep |= 0xFFFF0000u;
+    v[wd] &= keep;
+  }
+  return v;
+}
+
+// Zero the bytes e of a 16-byte chunk whose key index first + e >= limit.
+__device__ __forceinline__ u32x4 zero_bytes_from(u32x4 v, int first, int limit) {
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (first + 4 * wd + b < limit) keep |= 0xFFu << (8 * b);
     v[wd] &= keep;
   }
   return v;
@@ -141,19 +177,24 @@ __device__ __forceinline__ int kswz_rows(int r) {
   return ((x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1)) & (KCH - 1);
 }
 
-template <int DT, int D, int G>
+template <int DT, int KVT, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   using MM = Mfma<DT>;
   using vec8 = typename MM::vec8;
+  constexpr bool F8 = KVT == kFP8;        // pools hold E4M3 codes, widened to DT in registers
+  constexpr int EB = F8 ? 1 : 2;          // bytes of a stored K / V element
   constexpr int KS = D / 16;              // k-steps of K.Q^T
   constexpr int MBD = D / 32;             // 32-dim blocks of O^T
   constexpr int KT = 64;                  // keys per tile (four blocks)
   constexpr int TOKW = 32 / G;            // tokens per wave
-  constexpr int BLK = 16 * D * 2;         // bytes of one block's K (or V) tile
+  constexpr int KROW = D * EB;            // bytes of one K row (one key)
+  constexpr int VROW = 16 * EB;           // bytes of one V dim row (16 keys)
+  constexpr int BLK = 16 * KROW;          // bytes of one block's K (or V) tile
   constexpr int STAGE = 4 * BLK;          // one 64-key tile of K (or V)
   constexpr int NI = BLK / 1024;          // 1 KB LDS-DMA loads per block and tensor
-  constexpr int KCH = D / 8;              // 16-byte chunks per K row
-  constexpr int RPI = 1024 / (2 * D);     // K rows per DMA load
+  constexpr int KCH = KROW / 16;          // 16-byte chunks per K row
+  constexpr int RPI = 1024 / KROW;        // K rows per DMA load
+  static_assert(KVT == DT || F8, "stored K / V are the query type or E4M3 codes");
   constexpr int OROW = D * 4 + 16;        // epilogue: fp32 output row
   constexpr int OBYTES = 128 * OROW;
   constexpr int PIPE = 4 * STAGE;         // K stages 0,1 then V stages 0,1
@@ -213,17 +254,23 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 
   // ---- LDS-DMA tile loads ---------------------------------------------------------------------
   // Wave w loads block w of each tile, K and V, with NI buffer loads of 1 KB each straight into
-  // LDS (lane l lands at +16 l).  K stage: row t (0..63) at t * 2D, chunk c in slot c ^ kswz(t).
-  // V stage: block b at b * BLK as [D][16]; the two 16-byte halves of dim row d are swapped when
-  // vswz(d) is set.  Source offsets inside a block tile depend only on the lane: computed once.
+  // LDS (lane l lands at +16 l).  K stage: row t (0..63) at t * KROW, chunk c in slot
+  // c ^ kswz(t).  V stage: block b at b * BLK as [D][16]; for 2-byte elements the two 16-byte
+  // halves of dim row d are swapped when vswz(d) is set (a dim row of E4M3 codes is one
+  // 16-byte chunk and stays in place).  Source offsets inside a block tile depend only on the
+  // lane: computed once.
   const const_i32_ptr bt = as_const(a.block_tables) + (size_t)r * a.bt_stride;
   uint32_t koff[NI], voff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int t16 = j * RPI + lane / KCH;
-    koff[j] = (uint32_t)(t16 * 2 * D + ((lane % KCH) ^ kswz_rows<KCH>(t16)) * 16);
-    const int d = j * 32 + lane / 2;
-    voff[j] = (uint32_t)(d * 32 + ((lane & 1) ^ vswz(d)) * 16);
+    koff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ kswz_rows<KCH>(t16)) * 16);
+    if constexpr (F8) {
+      voff[j] = (uint32_t)((j * 64 + lane) * 16);
+    } else {
+      const int d = j * 32 + lane / 2;
+      voff[j] = (uint32_t)(d * 32 + ((lane & 1) ^ vswz(d)) * 16);
+    }
   }
   // Physical blocks this wave loads for tiles 0..127, held one per lane (lane l: tiles l and
   // 64 + l) and read with v_readlane, so that no scalar-load latency sits on the per-tile
@@ -258,14 +305,25 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // LDS row of the K key that MFMA row (32 mb + n) multiplies: bits 2 and 3 swapped.
   const int krow_of_n = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  // Per-lane LDS read offsets, fixed for the whole item.  K: row (32 mb + krow_of_n) and
-  // chunk (2 ks + h2) live at krd[ks] + 64 D mb inside a K stage.  V: dim row 32 j + n, half
-  // h2 of block ks lives at vrd + 1024 j + BLK ks inside a V stage (vswz(32 j + n) = vswz(n)).
+  // Per-lane LDS read offsets, fixed for the whole item.  K: the 8 elements of row
+  // (32 mb + krow_of_n) at dims 16 ks + 8 h2 live at krd[ks] + 32 KROW mb inside a K stage
+  // (2-byte elements: chunk 2 ks + h2; E4M3: half h2 of chunk ks).  V: keys 8 h2 .. 8 h2 + 7 of
+  // dim row 32 j + n of block ks live at vrd + 32 VROW j + BLK ks inside a V stage
+  // (vswz(32 j + n) = vswz(n)).
   uint32_t krd[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    krd[ks] = (uint32_t)(krow_of_n * 2 * D + (((2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n)) * 16));
-  const uint32_t vrd = (uint32_t)(n * 32 + ((h2 ^ vswz(n)) * 16));
+  for (int ks = 0; ks < KS; ++ks) {
+    if constexpr (F8)
+      krd[ks] = (uint32_t)(krow_of_n * KROW + ((ks ^ kswz_rows<KCH>(krow_of_n)) * 16) + 8 * h2);
+    else
+      krd[ks] = (uint32_t)(krow_of_n * KROW + (((2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n)) * 16));
+  }
+  const uint32_t vrd = F8 ? (uint32_t)(n * VROW + 8 * h2) : (uint32_t)(n * 32 + ((h2 ^ vswz(n)) * 16));
+  // One 8-element MFMA operand from LDS: 16 bytes as is, or 8 E4M3 codes widened exactly.
+  auto operand = [&](const uint8_t* p) -> vec8 {
+    if constexpr (F8) return MM::from_e4m3(*reinterpret_cast<const u32x2*>(p));
+    else return __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(p));
+  };
 
   // S^T of one tile for this lane's row: s[mb][v] is key t0 + 32 mb + 16 (v / 8) + 8 h2 + v % 8.
   // K operands are read in batches of four k-steps for both 32-key halves, and the two
@@ -280,8 +338,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          kop[kk][mb] = __builtin_bit_cast(
-              vec8, *reinterpret_cast<const u32x4*>(ks_base + krd[k0 + kk] + mb * 64 * D));
+          kop[kk][mb] = operand(ks_base + krd[k0 + kk] + mb * 32 * KROW);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -326,10 +383,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
         const int row = tid + 256 * x;       // (block, dim row) pairs: 4 x D
         if (row < 4 * D) {
           const int b = row / D, d = row % D;
+          if constexpr (F8) {
+            u32x4* p = reinterpret_cast<u32x4*>(v_cur + b * BLK + d * VROW);
+            *p = zero_bytes_from(*p, t0 + 16 * b, t_valid);
+          } else {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4* p = reinterpret_cast<u32x4*>(v_cur + b * BLK + d * 32 + ((hh ^ vswz(d)) * 16));
-            *p = zero_keys_from(*p, t0 + 16 * b + 8 * hh, t_valid);
+            for (int hh = 0; hh < 2; ++hh) {
+              u32x4* p = reinterpret_cast<u32x4*>(v_cur + b * BLK + d * 32 + ((hh ^ vswz(d)) * 16));
+              *p = zero_keys_from(*p, t0 + 16 * b + 8 * hh, t_valid);
+            }
           }
         }
       }
@@ -389,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          vop[jj][ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(v_cur + vrd + (j0 + jj) * 1024 + ks * BLK));
+          vop[jj][ks] = operand(v_cur + vrd + (j0 + jj) * 32 * VROW + ks * BLK);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -406,7 +468,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 
   // ---- epilogue: normalise, stage rows in LDS, store coalesced -----------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if constexpr (F8) inv *= a.v_scale;
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
   __syncthreads();                            // every wave is done reading the pipeline stages
   {
@@ -463,28 +526,35 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int KVT, int D>
 static hipError_t launch_mfma_d(const AttnArgs& args, int group, hipStream_t stream) {
   dim3 grid(args.num_items), block(256);
   switch (group) {
-    case 1: PK_LAUNCH((attn_mfma_kernel<DT, D, 1>), grid, block, stream, args); break;
-    case 2: PK_LAUNCH((attn_mfma_kernel<DT, D, 2>), grid, block, stream, args); break;
-    case 4: PK_LAUNCH((attn_mfma_kernel<DT, D, 4>), grid, block, stream, args); break;
-    case 8: PK_LAUNCH((attn_mfma_kernel<DT, D, 8>), grid, block, stream, args); break;
-    case 16: PK_LAUNCH((attn_mfma_kernel<DT, D, 16>), grid, block, stream, args); break;
-    case 32: PK_LAUNCH((attn_mfma_kernel<DT, D, 32>), grid, block, stream, args); break;
+    case 1: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 1>), grid, block, stream, args); break;
+    case 2: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 2>), grid, block, stream, args); break;
+    case 4: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 4>), grid, block, stream, args); break;
+    case 8: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 8>), grid, block, stream, args); break;
+    case 16: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 16>), grid, block, stream, args); break;
+    case 32: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 32>), grid, block, stream, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int head_dim, int group, hipStream_t stream) {
+template <int DT, int KVT>
+static hipError_t launch_mfma_dt(const AttnArgs& args, int head_dim, int group, hipStream_t stream) {
+  return head_dim == 64 ? launch_mfma_d<DT, KVT, 64>(args, group, stream)
+                        : launch_mfma_d<DT, KVT, 128>(args, group, stream);
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group,
+                            hipStream_t stream) {
   if (args.num_items == 0) return hipSuccess;
-  if (dtype == kF16)
-    return head_dim == 64 ? launch_mfma_d<kF16, 64>(args, group, stream) : launch_mfma_d<kF16, 128>(args, group, stream);
-  if (dtype == kBF16)
-    return head_dim == 64 ? launch_mfma_d<kBF16, 64>(args, group, stream)
-                          : launch_mfma_d<kBF16, 128>(args, group, stream);
+  const bool f8 = kv_dtype == kFP8;
+  if (dtype == kF16) return f8 ? launch_mfma_dt<kF16, kFP8>(args, head_dim, group, stream)
+                               : launch_mfma_dt<kF16, kF16>(args, head_dim, group, stream);
+  if (dtype == kBF16) return f8 ? launch_mfma_dt<kBF16, kFP8>(args, head_dim, group, stream)
+                                : launch_mfma_dt<kBF16, kBF16>(args, head_dim, group, stream);
   return hipErrorInvalidValue;
 }
 

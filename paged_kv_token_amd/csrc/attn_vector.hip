@@ -26,10 +26,40 @@
 
 namespace pk {
 
-template <int DT, int D, int NQ>
+// 16 E4M3 codes widened exactly to 8 packed pairs of the query type.
+template <int DT>
+__device__ __forceinline__ void widen_e4m3x16(const u32x4 w, uint32_t* pairs) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = w[i];
+    if constexpr (DT == kF16) {
+      pairs[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false));
+      pairs[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true));
+    } else {
+      pairs[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+      pairs[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
+    }
+  }
+}
+
+// acc + a.x * b.x + a.y * b.y over packed pairs of the query type, in fp32.
+template <int DT>
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
+  if constexpr (DT == kF16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), acc, false);
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), acc, false);
+  }
+}
+
+template <int DT, int KT, int D, int NQ>
 __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
-  constexpr int EB = DTypeInfo<DT>::bytes;
-  constexpr int EPC = 16 / EB;          // elements per 16-byte chunk
+  constexpr int EQ = DTypeInfo<DT>::bytes;   // bytes of a Q / O element
+  constexpr int EB = DTypeInfo<KT>::bytes;   // bytes of a stored K / V element
+  constexpr int EPC = 16 / EB;          // K / V elements per 16-byte chunk
+  constexpr int QCH = EPC * EQ / 16;    // 16-byte Q chunks matching one K chunk
   constexpr int LPT = D * EB / 16;      // lanes holding one K token row
   constexpr int TPI = 64 / LPT;         // K tokens per load
   constexpr int KI = 16 / TPI;          // K loads per block
@@ -38,6 +68,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   constexpr int VI = D / DPI;           // V loads per block
   constexpr int NW = 4;
   constexpr size_t TILE = (size_t)16 * D * EB;
+  static_assert(KT == DT || KT == kFP8, "stored K / V are the query type or E4M3 codes");
   static_assert(LPT >= 1 && LPT <= 32, "unsupported row width");
 
   __shared__ __attribute__((aligned(16))) float s_p[NW][NQ][16];
@@ -59,7 +90,11 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   const float c = a.scale_log2;
 
   // ---- query vectors and their positions -----------------------------------
-  float qv[NQ][EPC];
+  // Float pools: the lane's query elements as floats.  E4M3 pools: kept packed (two elements
+  // per register) and multiplied with the widened codes by two-element dot products.
+  constexpr bool F8 = KT == kFP8;
+  float qv[NQ][F8 ? 1 : EPC];
+  uint32_t qh[NQ][F8 ? EPC / 2 : 1];
   int qpos[NQ];
   int pmin = 0x7fffffff, pmax = -1;
   const int dim0 = (lane % LPT) * EPC;
@@ -69,8 +104,16 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
     const int tok = valid ? n / hc : 0;
     const int h = g * G + it.head_begin + (valid ? n % hc : 0);
     const int row = row0 + it.q_begin + tok;
-    const u32x4 qw = *reinterpret_cast<const u32x4*>(a.q + (((size_t)row * Hq + h) * D + dim0) * EB);
-    unpack16<DT>(qw, qv[n]);
+#pragma unroll
+    for (int qc = 0; qc < QCH; ++qc) {
+      const u32x4 qw = *reinterpret_cast<const u32x4*>(a.q + (((size_t)row * Hq + h) * D + dim0) * EQ + qc * 16);
+      if constexpr (F8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qh[n][4 * qc + e] = qw[e];
+      } else {
+        unpack16<DT>(qw, qv[n] + qc * (16 / EQ));
+      }
+    }
     int p = -1;
     if (valid) p = a.q_pos ? a.q_pos[row] : (L - q_r + it.q_begin + tok);
     qpos[n] = p;
@@ -108,14 +151,26 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
     float sc[NQ][KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-      float kf[EPC];
-      unpack16<DT>(kr[i], kf);
+      if constexpr (F8) {
+        uint32_t kp[EPC / 2];
+        widen_e4m3x16<DT>(kr[i], kp);
 #pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        float s = 0.f;
+        for (int n = 0; n < NQ; ++n) {
+          float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) s = fmaf(qv[n][e], kf[e], s);
-        sc[n][i] = group_sum<LPT>(s);
+          for (int e = 0; e < EPC / 2; ++e) s = dot2_acc<DT>(qh[n][e], kp[e], s);
+          sc[n][i] = group_sum<LPT>(s);
+        }
+      } else {
+        float kf[EPC];
+        unpack16<KT>(kr[i], kf);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) s = fmaf(qv[n][e], kf[e], s);
+          sc[n][i] = group_sum<LPT>(s);
+        }
       }
     }
     if (need_mask) {
@@ -153,7 +208,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
       float vf[EPC];
-      unpack16<DT>(vr[j], vf);
+      unpack16<KT>(vr[j], vf);
       if (zero_tail) {
 #pragma unroll
         for (int e = 0; e < EPC; ++e) vf[e] = (base + tc + e < L) ? vf[e] : 0.f;
@@ -216,6 +271,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
         o += f * s_acc[ww][n][d];
       }
       o /= lsum;
+      if constexpr (KT == kFP8) o *= a.v_scale;
     }
     const int tok = n / hc;
     const int h = g * G + it.head_begin + n % hc;
@@ -233,30 +289,34 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   }
 }
 
-template <int DT, int D>
+template <int DT, int KT, int D>
 static hipError_t launch_vec_d(const AttnArgs& args, int rows, hipStream_t stream) {
   dim3 grid(args.num_items), block(256);
   switch (rows) {
-    case 1: PK_LAUNCH((attn_vector_kernel<DT, D, 1>), grid, block, stream, args); break;
-    case 2: PK_LAUNCH((attn_vector_kernel<DT, D, 2>), grid, block, stream, args); break;
-    case 4: PK_LAUNCH((attn_vector_kernel<DT, D, 4>), grid, block, stream, args); break;
-    default: PK_LAUNCH((attn_vector_kernel<DT, D, 8>), grid, block, stream, args); break;
+    case 1: PK_LAUNCH((attn_vector_kernel<DT, KT, D, 1>), grid, block, stream, args); break;
+    case 2: PK_LAUNCH((attn_vector_kernel<DT, KT, D, 2>), grid, block, stream, args); break;
+    case 4: PK_LAUNCH((attn_vector_kernel<DT, KT, D, 4>), grid, block, stream, args); break;
+    default: PK_LAUNCH((attn_vector_kernel<DT, KT, D, 8>), grid, block, stream, args); break;
   }
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, int KT>
 static hipError_t launch_vec_dt(const AttnArgs& args, int head_dim, int rows, hipStream_t stream) {
-  return head_dim == 64 ? launch_vec_d<DT, 64>(args, rows, stream) : launch_vec_d<DT, 128>(args, rows, stream);
+  return head_dim == 64 ? launch_vec_d<DT, KT, 64>(args, rows, stream) : launch_vec_d<DT, KT, 128>(args, rows, stream);
 }
 
-hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int head_dim, int rows_per_item,
+hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int rows_per_item,
                               hipStream_t stream) {
   if (args.num_items == 0) return hipSuccess;
+  if (kv_dtype == kFP8) {
+    return dtype == kF16 ? launch_vec_dt<kF16, kFP8>(args, head_dim, rows_per_item, stream)
+                         : launch_vec_dt<kBF16, kFP8>(args, head_dim, rows_per_item, stream);
+  }
   switch (dtype) {
-    case kF32: return launch_vec_dt<kF32>(args, head_dim, rows_per_item, stream);
-    case kF16: return launch_vec_dt<kF16>(args, head_dim, rows_per_item, stream);
-    default: return launch_vec_dt<kBF16>(args, head_dim, rows_per_item, stream);
+    case kF32: return launch_vec_dt<kF32, kF32>(args, head_dim, rows_per_item, stream);
+    case kF16: return launch_vec_dt<kF16, kF16>(args, head_dim, rows_per_item, stream);
+    default: return launch_vec_dt<kBF16, kBF16>(args, head_dim, rows_per_item, stream);
   }
 }
 

@@ -6,11 +6,12 @@
 
 namespace pk {
 
-enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+// kFP8: OCP E4M3 codes (pool storage only; decoded value times the pool's scale).
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8 = 3 };
 
 template <int DT>
 struct DTypeInfo {
-  static constexpr int bytes = (DT == kF32) ? 4 : 2;
+  static constexpr int bytes = (DT == kF32) ? 4 : (DT == kFP8) ? 1 : 2;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -50,8 +51,9 @@ struct AttnArgs {
   int32_t bt_stride;
   int32_t part_stride;       // P of the partial buffers
   int32_t write_partials;    // 1: every item writes (m, l, O_p); 0: items with num_parts == 1 write O
-  float scale;               // softmax scale on q.k
+  float scale;               // scale on q.k as stored (softmax scale times the K pool's scale)
   float scale_log2;          // scale * log2(e)
+  float v_scale;             // scale of the V pool's stored values (1 for float pools)
 };
 
 // ---- element conversion ----------------------------------------------------
@@ -86,13 +88,34 @@ __device__ __forceinline__ void unpack16(const u32x4 w, float* out) {
       out[2 * i] = f16_bits_to_f32(w[i] & 0xFFFFu);
       out[2 * i + 1] = f16_bits_to_f32(w[i] >> 16);
     }
-  } else {
+  } else if constexpr (DT == kBF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[2 * i] = __builtin_bit_cast(float, w[i] << 16);
       out[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
     }
+  } else {
+    // E4M3 codes, decoded exactly by the hardware conversion (two per instruction).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = w[i];
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      out[4 * i] = lo[0];
+      out[4 * i + 1] = lo[1];
+      out[4 * i + 2] = hi[0];
+      out[4 * i + 3] = hi[1];
+    }
   }
+}
+
+// E4M3 code pair of two values already divided by the pool scale: magnitudes beyond 448 (the
+// largest finite E4M3 value) saturate, NaN stays NaN, the rest round to nearest even.  The pair
+// lands in the low (HI = false) or high half of `old`.
+__device__ __forceinline__ float e4m3_saturate(float x) { return fabsf(x) > 448.f ? copysignf(448.f, x) : x; }
+template <bool HI>
+__device__ __forceinline__ uint32_t pack_e4m3x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a), e4m3_saturate(b), (int)old, HI);
 }
 
 template <int DT>

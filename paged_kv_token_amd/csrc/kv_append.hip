@@ -111,4 +111,103 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pool, 
                         : launch_append<2, 128>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads, stream);
 }
 
+// FP8 append ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3): the KV cache stored as
+// 8-bit floats).  New rows arrive as f16 / bf16; each value is divided by its pool's scale
+// (float32, correctly rounded) and rounded to the nearest E4M3 code, saturating at 448.  Same
+// tiling as above: K rows go straight to their slots as 16-code chunks; V codes are staged in
+// LDS and written as 4-byte runs of 4 consecutive tokens of one dim row where the slots allow
+// (the pools' V tiles hold 16 one-byte tokens per dim row), else byte by byte.
+template <int SDT, int D>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(const uint8_t* __restrict__ k_new,
+                                                            const uint8_t* __restrict__ v_new,
+                                                            uint8_t* __restrict__ k_pool,
+                                                            uint8_t* __restrict__ v_pool,
+                                                            const int32_t* __restrict__ slots, int num_tokens,
+                                                            int num_kv_heads, float k_scale, float v_scale) {
+  constexpr int IN_ROW = D * 2;      // bytes of one token's input row for one head
+  constexpr int CPR = D / 16;        // 16-code chunks per token row
+  __shared__ int s_slot[16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[16 * D];
+
+  const int t0 = blockIdx.x * 16;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid < 16) s_slot[tid] = (t0 + tid < num_tokens) ? slots[t0 + tid] : -1;
+  __syncthreads();
+
+  const size_t tile_bytes = (size_t)16 * D;
+  for (int c = tid; c < 16 * CPR; c += 256) {
+    const int tok = c / CPR, wc = c % CPR;
+    const int s = s_slot[tok];
+    if (s < 0) continue;
+    const size_t src = ((size_t)(t0 + tok) * num_kv_heads + g) * IN_ROW + (size_t)wc * 32;
+    float kf[16], vf[16];
+    unpack16<SDT>(*reinterpret_cast<const u32x4*>(k_new + src), kf);
+    unpack16<SDT>(*reinterpret_cast<const u32x4*>(k_new + src + 16), kf + 8);
+    unpack16<SDT>(*reinterpret_cast<const u32x4*>(v_new + src), vf);
+    unpack16<SDT>(*reinterpret_cast<const u32x4*>(v_new + src + 16), vf + 8);
+    u32x4 kc, vc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t kw = pack_e4m3x2<false>(__fdiv_rn(kf[4 * i], k_scale), __fdiv_rn(kf[4 * i + 1], k_scale), 0u);
+      kc[i] = pack_e4m3x2<true>(__fdiv_rn(kf[4 * i + 2], k_scale), __fdiv_rn(kf[4 * i + 3], k_scale), kw);
+      const uint32_t vw = pack_e4m3x2<false>(__fdiv_rn(vf[4 * i], v_scale), __fdiv_rn(vf[4 * i + 1], v_scale), 0u);
+      vc[i] = pack_e4m3x2<true>(__fdiv_rn(vf[4 * i + 2], v_scale), __fdiv_rn(vf[4 * i + 3], v_scale), vw);
+    }
+    const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+    *reinterpret_cast<u32x4*>(k_pool + (blk * num_kv_heads + g) * tile_bytes + off * D + (size_t)wc * 16) = kc;
+    *reinterpret_cast<u32x4*>(s_v + tok * D + wc * 16) = vc;
+  }
+  __syncthreads();
+
+  for (int c = tid; c < D * 4; c += 256) {
+    const int ts = (c % 4) * 4, d = c / 4;
+    const int s0 = s_slot[ts];
+    bool run = (s0 >= 0) && (s0 % 4) == 0;
+#pragma unroll
+    for (int e = 1; e < 4; ++e) run = run && (s_slot[ts + e] == s0 + e);
+    if (run) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) word |= (uint32_t)s_v[(ts + e) * D + d] << (8 * e);
+      const size_t blk = (size_t)(s0 >> 4), off = (size_t)(s0 & 15);
+      *reinterpret_cast<uint32_t*>(v_pool + (blk * num_kv_heads + g) * tile_bytes + (size_t)d * 16 + off) = word;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = s_slot[ts + e];
+        if (s < 0) continue;
+        const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
+        v_pool[(blk * num_kv_heads + g) * tile_bytes + (size_t)d * 16 + off] = s_v[(ts + e) * D + d];
+      }
+    }
+  }
+}
+
+template <int SDT, int D>
+static hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                    const int32_t* slots, int num_tokens, int num_kv_heads, float k_scale,
+                                    float v_scale, hipStream_t stream) {
+  dim3 grid((num_tokens + 15) / 16, num_kv_heads);
+  PK_LAUNCH((kv_append_fp8_kernel<SDT, D>), grid, dim3(256), stream, static_cast<const uint8_t*>(k_new),
+            static_cast<const uint8_t*>(v_new), static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slots,
+            num_tokens, num_kv_heads, k_scale, v_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim, int src_dtype,
+                                float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  if (src_dtype == kF16)
+    return head_dim == 64 ? launch_append_fp8<kF16, 64>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads,
+                                                        k_scale, v_scale, stream)
+                          : launch_append_fp8<kF16, 128>(k_new, v_new, k_pool, v_pool, slots, num_tokens,
+                                                         num_kv_heads, k_scale, v_scale, stream);
+  return head_dim == 64 ? launch_append_fp8<kBF16, 64>(k_new, v_new, k_pool, v_pool, slots, num_tokens, num_kv_heads,
+                                                       k_scale, v_scale, stream)
+                        : launch_append_fp8<kBF16, 128>(k_new, v_new, k_pool, v_pool, slots, num_tokens,
+                                                        num_kv_heads, k_scale, v_scale, stream);
+}
+
 }  // namespace pk

@@ -32,14 +32,20 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_pool, 
                             const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim,
                             int elem_bytes, hipStream_t stream);
 
+// New f16 / bf16 K/V rows rounded to E4M3 codes (value / scale) into FP8 pools.
+hipError_t launch_kv_append_fp8(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                const int32_t* slots, int num_tokens, int num_kv_heads, int head_dim, int src_dtype,
+                                float k_scale, float v_scale, hipStream_t stream);
+
 // Vector-ALU attention: items of at most `rows_per_item` query vectors
 // (tokens x heads of one KV group).  rows_per_item in {1, 2, 4, 8}.
-hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int head_dim, int rows_per_item,
+hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int rows_per_item,
                               hipStream_t stream);
 
 // Matrix-core attention: items of up to 128 query vectors (tokens x the
 // whole head group), fp16/bf16 only.
-hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int head_dim, int group, hipStream_t stream);
+hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group,
+                            hipStream_t stream);
 
 // Copy n whole blocks (K and V runs of block_bytes each) from src to dst pools; pairs holds n
 // {source block, destination block} pairs.  Either side may be device-mapped host memory.

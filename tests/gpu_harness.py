@@ -61,44 +61,60 @@ class GpuBatch:
     cu_q_lens: object
     q_pos: Optional[object]
     desc: object
+    kv_fp8: Optional[tuple] = None     # (k_scale, v_scale) when the pools hold E4M3 codes
 
     def make_desc(self, flags: int = 0):
         b = self.batch
+        fp8 = {} if self.kv_fp8 is None else dict(kv_dtype=pk.PENSIEVE_FP8_E4M3, k_scale=self.kv_fp8[0],
+                                                   v_scale=self.kv_fp8[1])
         return pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                             num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
                             dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
-                            context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens, flags=flags)
+                            context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens, flags=flags, **fp8)
 
 
 def upload(batch: Batch, *, append_new: bool = True, poison: bool = True, pass_q_pos: Optional[bool] = None,
-           chunk_tokens: int = 1 << 16) -> GpuBatch:
-    """Pools filled through pensieve_kv_append: cached history first, then (optionally) the new rows."""
+           chunk_tokens: int = 1 << 16, kv_fp8: Optional[tuple] = None) -> GpuBatch:
+    """Pools filled through pensieve_kv_append: cached history first, then (optionally) the new rows.
+
+    kv_fp8 = (k_scale, v_scale): E4M3 pools (uint8) filled through pensieve_kv_append_fp8;
+    poison is then the NaN code 0x7F.
+    """
     import torch
     b = batch
-    td = torch_dtype(b.dtype)
+    td = torch.uint8 if kv_fp8 is not None else torch_dtype(b.dtype)
     k_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.block_size, b.head_dim), dtype=td, device="cuda")
     v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size), dtype=td, device="cuda")
-    if poison:
+    if kv_fp8 is not None:
+        k_pool.fill_(0x7F if poison else 0); v_pool.fill_(0x7F if poison else 0)
+    elif poison:
         poison_(k_pool, b.dtype); poison_(v_pool, b.dtype)
     else:
         k_pool.zero_(); v_pool.zero_()
+
+    def append(kk, vv, ss):
+        if kv_fp8 is None:
+            pk.pensieve_kv_append(kk, vv, k_pool, v_pool, ss)
+        else:
+            pk.pensieve_kv_append_fp8(kk, vv, k_pool, v_pool, ss, kv_fp8[0], kv_fp8[1])
+
     for r, k, v, slots, pos in b.iter_requests():
         for lo in range(0, len(pos), chunk_tokens):
             sel = pos[lo:lo + chunk_tokens]
             kk = to_device(k[sel], b.dtype); vv = to_device(v[sel], b.dtype)
             ss = torch.from_numpy(slots[lo:lo + chunk_tokens].copy()).cuda()
-            pk.pensieve_kv_append(kk, vv, k_pool, v_pool, ss)
+            append(kk, vv, ss)
     k_new_np, v_new_np = b.new_kv()
     k_new = to_device(k_new_np, b.dtype); v_new = to_device(v_new_np, b.dtype)
     new_slots = torch.from_numpy(b.new_slots.copy()).cuda()
     if append_new:
-        pk.pensieve_kv_append(k_new, v_new, k_pool, v_pool, new_slots)
+        append(k_new, v_new, new_slots)
     use_qpos = (not b.has_default_positions) if pass_q_pos is None else pass_q_pos
     gb = GpuBatch(b, k_pool, v_pool, to_device(b.q_all(), b.dtype), k_new, v_new, new_slots,
                   torch.from_numpy(b.block_tables.copy()).cuda(),
                   torch.from_numpy(b.context_lens.copy()).cuda(),
                   torch.from_numpy(b.cu_q_lens.copy()).cuda(),
-                  torch.from_numpy(b.q_pos.copy()).cuda() if use_qpos else None, None)
+                  torch.from_numpy(b.q_pos.copy()).cuda() if use_qpos else None, None, kv_fp8)
     gb.desc = gb.make_desc()
     torch.cuda.synchronize()
     return gb

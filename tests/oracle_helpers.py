@@ -14,23 +14,34 @@ def poison_fill(dtype: str):
     return BF16_NAN if dtype == "bf16" else np.nan
 
 
-def oracle_pools(batch: Batch, impl=oracle, poison=True, include_new=True):
+def oracle_pools(batch: Batch, impl=oracle, poison=True, include_new=True, kv_fp8=None):
     """Pools [NB][Hkv][B][d] (K) and [NB][Hkv][d][B] (V) filled through ``impl.append_kv``.
 
     Every slot starts as NaN (poison), then cached history and (optionally)
-    the step's new rows are appended.
+    the step's new rows are appended.  kv_fp8 = (k_scale, v_scale): the pools
+    hold E4M3 codes (uint8) of the rows divided by the scales.
     """
-    sd = storage_dtype(batch.dtype)
     nb, hkv, B, d = batch.num_blocks, batch.num_kv_heads, batch.block_size, batch.head_dim
-    fill = poison_fill(batch.dtype) if poison else 0
+    if kv_fp8 is None:
+        sd, fill = storage_dtype(batch.dtype), (poison_fill(batch.dtype) if poison else 0)
+        enc_k = enc_v = lambda x: x
+    else:
+        sd, fill = np.uint8, (0x7F if poison else 0)
+        enc_k = lambda x: oracle.quantize_e4m3(x, batch.dtype, kv_fp8[0])
+        enc_v = lambda x: oracle.quantize_e4m3(x, batch.dtype, kv_fp8[1])
     k_pool = np.full((nb, hkv, B, d), fill, dtype=sd)
     v_pool = np.full((nb, hkv, d, B), fill, dtype=sd)
     for r, k, v, slots, pos in batch.iter_requests():
-        impl.append_kv(k_pool, v_pool, k[pos], v[pos], slots, B)
+        impl.append_kv(k_pool, v_pool, enc_k(k[pos]), enc_v(v[pos]), slots, B)
     if include_new:
         k_new, v_new = batch.new_kv()
-        impl.append_kv(k_pool, v_pool, k_new, v_new, batch.new_slots, B)
+        impl.append_kv(k_pool, v_pool, enc_k(k_new), enc_v(v_new), batch.new_slots, B)
     return k_pool, v_pool
+
+
+def fp8_kw(kv_fp8):
+    """Keyword arguments of the oracle's attention for E4M3 pools with scales kv_fp8."""
+    return {} if kv_fp8 is None else dict(kv_dtype="e4m3", k_scale=kv_fp8[0], v_scale=kv_fp8[1])
 
 
 def batch_q_pos(batch: Batch):

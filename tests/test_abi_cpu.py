@@ -57,6 +57,11 @@ def desc_for(b, **over):
     (dict(context_lens_host=[4, 5, 6], cu_q_lens_host=[1, 2, 3, 4]), 1),   # cu[0] != 0
     (dict(context_lens_host=[4, 5, 6], cu_q_lens_host=[0, 2, 1, 2]), 1),   # decreasing
     (dict(context_lens_host=[4, -1, 6], cu_q_lens_host=[0, 1, 1, 2]), 1),
+    (dict(kv_dtype=0), 2),                                   # f32 pools under f16 queries
+    (dict(kv_dtype=9), 2),
+    (dict(kv_dtype=3, k_scale=0.0), 1), (dict(kv_dtype=3, v_scale=float("inf")), 1),
+    (dict(kv_dtype=3, k_scale=float("nan")), 1), (dict(kv_dtype=3, v_scale=-1.0), 1),
+    (dict(dtype=0, kv_dtype=3), 2),                          # E4M3 pools need f16 / bf16 queries
 ])
 def test_bad_descriptors_are_rejected(lib, over, status):
     b = custom_batch([10, 20, 30], [1, 2, 3], num_heads=4, num_kv_heads=2, head_dim=64, dtype="f16", seed=1)
@@ -246,3 +251,20 @@ def test_kv_swap_rejects_bad_arguments_before_any_launch(lib, direction, case, s
 
 def test_kv_swap_of_nothing_is_a_no_op(lib):
     assert lib.pensieve_kv_swap_in(None, None, 1, None, None, 1, None, None, 0, 4, 64, 1, None) == 0
+
+
+def test_fp8_descriptor_is_accepted(lib):
+    b = custom_batch([10, 20, 30], [1, 2, 3], num_heads=4, num_kv_heads=2, head_dim=64, dtype="bf16", seed=1)
+    assert pk.pensieve_attn_workspace_size(desc_for(b, kv_dtype=3, k_scale=0.5, v_scale=2.0)) > 0
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(src=0), 2), (dict(src=3), 2), (dict(ks=0.0), 1), (dict(vs=float("nan")), 1), (dict(d=80), 2),
+    (dict(n=-1), 1), (dict(n=4), 1),                         # NULL pointers with work to do
+])
+def test_fp8_append_rejects_bad_arguments(lib, args, status):
+    a = dict(src=1, ks=1.0, vs=1.0, d=64, n=0)
+    a.update(args)
+    st = lib.pensieve_kv_append_fp8(None, None, None, None, None, a["n"], 2, a["d"], 16, 10, a["src"], a["ks"],
+                                    a["vs"], None)
+    assert st == status
