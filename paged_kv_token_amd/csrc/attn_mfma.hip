@@ -347,6 +347,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   };
 
   f32x16 s_cur[2], s_nxt[2];
+  // A wave whose 32 query vectors all lie past the item's rows (short prefill items) still
+  // loads its share of every tile and meets every barrier, but computes nothing.
+  const bool wave_idle = uniform(w * TOKW >= it.q_count ? 1 : 0) != 0;
   wait_vmem_all();                           // query rows and positions have landed
   if (ntiles > 0) {
     issue(a.k_pool, koff, 0, kstage(0));
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
     lds_barrier();
-    qk(lds, s_cur);
+    if (!wave_idle) qk(lds, s_cur);
   }
 
   // One tile: PAR is ti & 1 (the K stage of tile ti + 1 and the V stage of tile ti are
@@ -398,6 +401,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
       lds_barrier();
     }
+    if (wave_idle) return;                    // loads and barriers only
     // Masking (diagonal and tail tiles only): key offset 32 mb + 16 (v / 8) + v % 8 from
     // t0 + 8 h2 is visible iff it is <= lim.
     if ((t0 + KT - 1 > pmin_w) || (t0 + KT > t_valid)) {
