@@ -89,8 +89,10 @@ typedef enum pensieve_dtype {
 } pensieve_dtype;
 
 /* pensieve_batch_desc.flags: route every work item to the vector-ALU kernel
- * (the matrix-core kernel is otherwise used for items with many query rows
- * on F16/BF16).  Results agree within the stated tolerances either way. */
+ * (on F16/BF16 the matrix-core kernel otherwise serves requests with more
+ * than 8 query vectors (rows x heads per KV head) and every request of head
+ * groups of 4 or more).  Results agree within the stated tolerances either
+ * way. */
 #define PENSIEVE_FLAG_VECTOR_ONLY 1
 
 /* Shape of one unified batch plus host copies of its lengths (used to

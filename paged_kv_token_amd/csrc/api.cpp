@@ -57,6 +57,10 @@ pensieve_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int kBlockSize = 16;
 constexpr int kVectorRowsMax = 8;    // query vectors per vector-kernel item
+// Head groups of this size or more always run on the matrix cores: the matrix-core kernel
+// streams a GQA group's K/V at 4.8 TB/s for one decode token (G = 8), where the vector kernel,
+// holding eight query vectors per lane group, reaches 1.8 TB/s.
+constexpr int kMatrixMinGroup = 4;
 constexpr int kMfmaRows = 128;       // query vectors per matrix-core item
 constexpr int kMaxPartitions = 256;
 // Adaptive split-KV of pensieve_attn_fwd: the plan aims at about kSplitTargetItems work
@@ -217,6 +221,11 @@ void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGrou
     for (int x = 0; x < kXcds; ++x) out.push_back(k < bins[x].size() ? items[bins[x][k]] : filler);
 }
 
+// Kernel of a request's items: the vector kernel for few query vectors of small head groups.
+bool routes_to_matrix(bool matrix_allowed, int q, int G) {
+  return matrix_allowed && ((long long)q * G > kVectorRowsMax || G >= kMatrixMinGroup);
+}
+
 // Work items of one request for one KV head and partition (no split): matrix-core items of
 // kMfmaRows query vectors, or vector items of at most kVectorRowsMax.
 long long items_per_kv_head(int q, int G, bool use_matrix) {
@@ -240,7 +249,7 @@ std::vector<int> choose_partitions(const pensieve_batch_desc* d, int num_partiti
     const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
     if (q == 0) continue;
     const long long nblk = (d->context_lens_host[r] + kBlockSize - 1) / kBlockSize;
-    const bool use_matrix = mat && (long long)q * G > kVectorRowsMax;
+    const bool use_matrix = routes_to_matrix(mat, q, G);
     total += items_per_kv_head(q, G, use_matrix) * d->num_kv_heads * (nblk + 1);
   }
   const long long share = std::max(kSplitMinBlocks, total / kSplitTargetItems);
@@ -298,7 +307,7 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
     const int P = parts[r];
     const long long nblk = (L + kBlockSize - 1) / kBlockSize;
     const long long per = (nblk + P - 1) / P;
-    const bool use_matrix = mat && (long long)q * G > kVectorRowsMax;
+    const bool use_matrix = routes_to_matrix(mat, q, G);
     for (int part = 0; part < P; ++part) {
       const long long blocks = std::max(0LL, std::min(per, nblk - part * per));
       for (int g = 0; g < d->num_kv_heads; ++g) {

@@ -191,6 +191,14 @@ def test_routing_rules(lib):
     assert np.all(plan_v[:, 0] == 0) and np.all(plan_v[:, 4] * plan_v[:, 9] <= 8)
     f32 = custom_batch([100], [50], num_heads=4, num_kv_heads=4, head_dim=64, dtype="f32", seed=2)
     assert np.all(pk.pensieve_debug_plan(desc_for(f32))[:, 0] == 0)
+    # Head groups of 4 or more go to the matrix cores even for one decode token; pairs stay on
+    # the vector kernel up to 8 query vectors.
+    for hq, hkv, want in ((16, 2, 1), (8, 2, 1), (4, 2, 0), (4, 4, 0)):
+        dec = custom_batch([300, 40, 0], [1, 1, 1], num_heads=hq, num_kv_heads=hkv, head_dim=128, dtype="bf16",
+                           seed=3)
+        live = pk.pensieve_debug_plan(desc_for(dec))
+        live = live[live[:, 4] > 0]
+        assert np.all(live[:, 0] == want), (hq, hkv)
 
 
 def test_workspace_size_matches_plan(lib):
