@@ -4,8 +4,9 @@
 // batch.  One workgroup (4 waves) handles one work item: up to NQ query
 // vectors (tokens x query heads of one KV head) of one request, over one
 // partition of that request's KV blocks.  The four waves stride over the
-// item's blocks; each wave keeps an online softmax per query vector in
-// registers and the waves merge through LDS at the end.
+// item's blocks, each with two blocks' loads in flight; each wave keeps an
+// online softmax per query vector in registers and the waves merge through
+// LDS at the end.
 //
 // Per 16-token block a wave issues 16-byte loads that cover the K tile
 // [16][D] and the V tile [D][16] exactly once (64 lanes x 16 B per load), so
@@ -225,19 +226,28 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   };
 
   {
-    u32x4 kc[KI], vc[VI];
-    int blk = kb0 + w;
+    // Two blocks in flight per wave: three register sets rotate by unrolling, and the loads
+    // of block b + 2 NW are issued before block b is processed.  Loads past the item's last
+    // block fetch that block again (unused, and still in L2), so every step issues the same
+    // loads and the compiler's wait counts stay exact.
+    u32x4 ka[KI], va[VI], kb[KI], vb[VI], kc[KI], vc[VI];
+    const int b0 = kb0 + w;
+    auto clamp_blk = [&](int b) { return b < kb1 ? b : kb1 - 1; };
     wait_vmem_all();
-    if (blk < kb1) load(blk, kc, vc);
-    for (; blk < kb1; blk += NW) {
-      u32x4 kn[KI] = {}, vn[VI] = {};
-      const int nb = blk + NW;
-      if (nb < kb1) load(nb, kn, vn);
-      process(blk, kc, vc);
-#pragma unroll
-      for (int i = 0; i < KI; ++i) kc[i] = kn[i];
-#pragma unroll
-      for (int j = 0; j < VI; ++j) vc[j] = vn[j];
+    if (b0 < kb1) {
+      load(b0, ka, va);
+      load(clamp_blk(b0 + NW), kb, vb);
+      for (int blk = b0; blk < kb1; blk += 3 * NW) {
+        load(clamp_blk(blk + 2 * NW), kc, vc);
+        process(blk, ka, va);
+        if (blk + NW >= kb1) break;
+        load(clamp_blk(blk + 3 * NW), ka, va);
+        process(blk + NW, kb, vb);
+        if (blk + 2 * NW >= kb1) break;
+        load(clamp_blk(blk + 4 * NW), kb, vb);
+        process(blk + 2 * NW, kc, vc);
+      }
+      wait_vmem_all();     // the unused loads of the last step have landed
     }
   }
 
