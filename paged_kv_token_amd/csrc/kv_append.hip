@@ -7,13 +7,72 @@
 // Pools: K [num_blocks][Hkv][16][D] (token rows), V [num_blocks][Hkv][D][16]
 // (dim rows).  One workgroup copies 16 consecutive new tokens of one KV head:
 // K rows go straight to their slots with 16-byte stores; V rows are staged in
-// LDS and written as 16-byte runs of consecutive tokens of one dim row when
-// the slots of a token run are consecutive and aligned (the usual case: a
-// request's new tokens fill its blocks in order), else one element at a time.
+// LDS and each run of consecutive slots (a request's new tokens fill its
+// blocks in order, usually starting mid-block) leaves in the widest aligned
+// stores its position allows.
 #include "device_common.h"
 #include "launch.h"
 
 namespace pk {
+
+// One element (EB bytes) read from LDS, zero-extended.
+template <int EB>
+__device__ __forceinline__ uint32_t lds_elem(const uint8_t* p) {
+  if constexpr (EB == 4) return *reinterpret_cast<const uint32_t*>(p);
+  else if constexpr (EB == 2) return *reinterpret_cast<const uint16_t*>(p);
+  else return *p;
+}
+
+// Store u (a power of two, u * EB <= 16, dst aligned to u * EB) elements gathered from
+// src, src + stride, ... with one store of u * EB bytes.
+template <int EB>
+__device__ __forceinline__ void store_elems(uint8_t* dst, const uint8_t* src, int stride, int u) {
+  constexpr int MAXU = 16 / EB, PER = 4 / EB;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < MAXU; ++i)
+    if (i < u) w[i / PER] |= lds_elem<EB>(src + i * stride) << (8 * EB * (i % PER));
+  switch (u * EB) {
+    case 16: *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]}; break;
+    case 8: *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]}; break;
+    case 4: *reinterpret_cast<uint32_t*>(dst) = w[0]; break;
+    case 2: *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0]; break;
+    default: *dst = (uint8_t)w[0]; break;
+  }
+}
+
+// V rows staged in LDS (16 token rows of D elements of EB bytes) to the dim-major V tiles of
+// their slots.  One thread per dim row walks the 16 tokens run by run -- a run is a stretch
+// of consecutive slots inside one block -- and writes each run with the widest aligned stores
+// (16, 8, 4, 2 or 1 bytes), so a run that starts mid-block still leaves in wide stores.
+template <int EB, int D>
+__device__ __forceinline__ void store_v_runs(const int* s_slot, const uint8_t* s_v, uint8_t* v_pool,
+                                             int num_kv_heads, int g, int tid) {
+  constexpr size_t TILE = (size_t)16 * D * EB;
+  constexpr int ROW = D * EB;
+  for (int d = tid; d < D; d += 256) {
+    int t = 0;
+    while (t < 16) {
+      const int s = s_slot[t];
+      if (s < 0) { ++t; continue; }
+      int n = 1;
+      while (t + n < 16 && s_slot[t + n] == s + n && ((s + n) & 15) != 0) ++n;
+      uint8_t* row = v_pool + ((size_t)(s >> 4) * num_kv_heads + g) * TILE + (size_t)d * 16 * EB;
+      int p = s & 15;
+      const int end = p + n;
+      const uint8_t* src = s_v + t * ROW + d * EB;
+      while (p < end) {
+        int u = 16 / EB;
+        while (u > 1 && ((p & (u - 1)) != 0 || p + u > end)) u >>= 1;
+        store_elems<EB>(row + p * EB, src, ROW, u);
+        src += u * ROW;
+        p += u;
+      }
+      t += n;
+    }
+  }
+}
+
 
 template <int EB, int D>
 __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ k_new,
@@ -24,8 +83,6 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
                                                         int num_kv_heads) {
   constexpr int ROW = D * EB;        // bytes of one token's row for one head
   constexpr int CPR = ROW / 16;      // 16-byte chunks per row
-  constexpr int EPC = 16 / EB;       // elements per 16-byte chunk
-  constexpr int TG = 16 / EPC;       // 16-byte token runs per V dim row
   __shared__ int s_slot[16];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[16 * ROW];
 
@@ -49,43 +106,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
   }
   __syncthreads();
 
-  for (int c = tid; c < D * TG; c += 256) {
-    const int tg = c % TG, d = c / TG;
-    const int ts = tg * EPC;
-    const int s0 = s_slot[ts];
-    bool run = (s0 >= 0) && (s0 % EPC) == 0;
-#pragma unroll
-    for (int e = 1; e < EPC; ++e) run = run && (s_slot[ts + e] == s0 + e);
-    if (run) {
-      u32x4 out;
-      if constexpr (EB == 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = *reinterpret_cast<const uint32_t*>(s_v + (ts + e) * ROW + d * 4);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(s_v + (ts + 2 * e) * ROW + d * 2);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(s_v + (ts + 2 * e + 1) * ROW + d * 2);
-          out[e] = lo | (hi << 16);
-        }
-      }
-      const size_t blk = (size_t)(s0 >> 4), off = (size_t)(s0 & 15);
-      *reinterpret_cast<u32x4*>(v_pool + (blk * num_kv_heads + g) * tile_bytes + (size_t)d * 16 * EB + off * EB) = out;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        const int s = s_slot[ts + e];
-        if (s < 0) continue;
-        const size_t blk = (size_t)(s >> 4), off = (size_t)(s & 15);
-        uint8_t* dst = v_pool + (blk * num_kv_heads + g) * tile_bytes + (size_t)d * 16 * EB + off * EB;
-        if constexpr (EB == 4) {
-          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(s_v + (ts + e) * ROW + d * 4);
-        } else {
-          *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(s_v + (ts + e) * ROW + d * 2);
-        }
-      }
-    }
-  }
+  store_v_runs<EB, D>(s_slot, s_v, v_pool, num_kv_heads, g, tid);
 }
 
 template <int EB, int D>
