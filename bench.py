@@ -357,6 +357,7 @@ def swap_measure(index: int = 1, reps: int = 5, steps: int = 40):
     steps_ms(0)
     alone = steps_ms(0)
     m = int(min(len(spare), 0.5 * alone * 1e-3 * (nbytes / (in_ms * 1e-3)) / block_bytes))
+    steps_ms(m)                                  # first use of the side stream and its launches
     beside = steps_ms(m)
     m_bytes = m * block_bytes
     out = {"workload": b.name, "blocks": n, "bytes": nbytes, "swap_out_ms": round(out_ms, 3),
