@@ -65,32 +65,42 @@ class OracleBackend:
 class GpuBackend:
     """Pools on the GPU, filled by pensieve_kv_append and read by pensieve_attn_fwd."""
 
+    kv_fp8 = None     # (k_scale, v_scale) for E4M3 pools
+
     def __init__(self, num_blocks, num_kv_heads, head_dim, dtype):
         import torch
         from gpu_harness import torch_dtype
-        td = torch_dtype(dtype)
+        td = torch.uint8 if self.kv_fp8 else torch_dtype(dtype)
+        self.poison = 0x7F if self.kv_fp8 else float("nan")
         self.dtype = dtype
         self.num_blocks = num_blocks
-        self.k_pool = torch.full((num_blocks, num_kv_heads, BLOCK, head_dim), float("nan"), dtype=td, device="cuda")
-        self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, BLOCK), float("nan"), dtype=td, device="cuda")
+        self.k_pool = torch.full((num_blocks, num_kv_heads, BLOCK, head_dim), self.poison, dtype=td, device="cuda")
+        self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, BLOCK), self.poison, dtype=td, device="cuda")
 
     def free(self, blocks):
         import torch
         idx = torch.as_tensor(np.asarray(blocks, dtype=np.int64), device="cuda")
-        self.k_pool[idx] = float("nan")
-        self.v_pool[idx] = float("nan")
+        self.k_pool[idx] = self.poison
+        self.v_pool[idx] = self.poison
+
+    def append(self, k, v, slots):
+        if self.kv_fp8:
+            pk.pensieve_kv_append_fp8(k, v, self.k_pool, self.v_pool, slots, *self.kv_fp8)
+        else:
+            pk.pensieve_kv_append(k, v, self.k_pool, self.v_pool, slots)
 
     def step(self, q, k_rows, v_rows, slots, block_tables, context_lens, cu_q_lens, q_pos, scale, num_heads):
         import torch
         from gpu_harness import to_device, to_f64
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
         qt = to_device(q, self.dtype)
-        pk.pensieve_kv_append(to_device(k_rows, self.dtype), to_device(v_rows, self.dtype), self.k_pool,
-                              self.v_pool, dev(slots))
+        self.append(to_device(k_rows, self.dtype), to_device(v_rows, self.dtype), dev(slots))
+        fp8 = {} if not self.kv_fp8 else dict(kv_dtype=pk.PENSIEVE_FP8_E4M3, k_scale=self.kv_fp8[0],
+                                               v_scale=self.kv_fp8[1])
         desc = pk.make_desc(num_heads=num_heads, num_kv_heads=self.k_pool.shape[1], head_dim=self.k_pool.shape[3],
                             num_blocks=self.num_blocks, block_table_stride=block_tables.shape[1],
                             dtype={"f32": 0, "f16": 1, "bf16": 2}[self.dtype], softmax_scale=scale,
-                            context_lens_host=context_lens, cu_q_lens_host=cu_q_lens)
+                            context_lens_host=context_lens, cu_q_lens_host=cu_q_lens, **fp8)
         ws = torch.empty(max(pk.pensieve_attn_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
         ws.fill_(0xFF)
         o = torch.full_like(qt, float("nan"))
@@ -98,6 +108,22 @@ class GpuBackend:
                              dev(cu_q_lens), dev(q_pos), o, ws)
         torch.cuda.synchronize()
         return to_f64(o)
+
+
+class GpuFp8Backend(GpuBackend):
+    """E4M3 pools (scales 1/64 for K, 1/48 for V) through pensieve_kv_append_fp8."""
+
+    kv_fp8 = (1 / 64, 1 / 48)
+
+
+def reference_kv(backend, x, dtype, which):
+    """Values the attention must see for stored rows x: the rows themselves, or for E4M3 pools
+    the decoded codes times the pool's scale."""
+    fp8 = getattr(backend, "kv_fp8", None)
+    if not fp8:
+        return oracle.to_f64(x, dtype)
+    scale = fp8[0] if which == "k" else fp8[1]
+    return oracle.e4m3_decode(oracle.quantize_e4m3(x, dtype, scale)) * scale
 
 
 def run(backend_cls, *, seed, num_convs, steps, num_blocks, num_heads, num_kv_heads, head_dim, dtype, tol,
@@ -167,8 +193,8 @@ def run(backend_cls, *, seed, num_convs, steps, num_blocks, num_heads, num_kv_he
                 for h in range(num_heads):
                     g = oracle.kv_head_of(h, num_heads, num_kv_heads)
                     ref = oracle.causal_attention(oracle.to_f64(q[lo:hi, h], dtype),
-                                                  oracle.to_f64(kv[c][0][:L, g], dtype),
-                                                  oracle.to_f64(kv[c][1][:L, g], dtype), pos, scale)
+                                                  reference_kv(backend, kv[c][0][:L, g], dtype, "k"),
+                                                  reference_kv(backend, kv[c][1][:L, g], dtype, "v"), pos, scale)
                     e = float(np.max(np.abs(got[lo:hi, h] - ref))) if hi > lo else 0.0
                     assert np.isfinite(e) and e <= tol, (t, int(c), h, e)
                     err = max(err, e)
