@@ -172,3 +172,40 @@ def test_fp8_swap_round_trip_leaves_attention_bitwise_unchanged():
     torch.cuda.synchronize()
     after = run_attn(gb)
     assert torch.equal(before.view(torch.int16), after.view(torch.int16))
+
+
+def test_fp8_pool_offsets_beyond_4_gib():
+    """Blocks placed past byte 2^32 of 4.6 GB E4M3 pools: append and both kernels must address them
+    with 64-bit offsets (reference: the oracle over each request's logical K/V, quantised)."""
+    import torch
+    nb = 300_000                                 # 8 KV heads x 16 x 128 bytes = 16 KiB per block
+    b = custom_batch([700, 1500, 33, 90], [1, 40, 5, 1], num_heads=16, num_kv_heads=8, head_dim=128,
+                     dtype="bf16", seed=77, num_blocks=nb)
+    bt = b.block_tables.copy()
+    top = nb - 1
+    for r in range(b.num_reqs):
+        n = b.num_logical_blocks(r)
+        bt[r, :n] = top - np.arange(n) * 7 - r   # descending ids near the end of the pool
+    used = np.concatenate([bt[r, :b.num_logical_blocks(r)] for r in range(b.num_reqs)])
+    assert len(np.unique(used)) == len(used)
+    b.block_tables = bt
+    assert (int(bt.max()) + 1) * 8 * 16 * 128 > 2 ** 32
+    gb = upload(b, kv_fp8=SCALES)
+    for path in sorted(PATHS):
+        got = to_f64(run_attn(gb, PATHS[path]))
+        q = b.q_all()
+        err = 0.0
+        for r in range(b.num_reqs):
+            k, v = b.request_kv(r)
+            lo, hi = int(b.cu_q_lens[r]), int(b.cu_q_lens[r + 1])
+            for h in range(b.num_heads):
+                g = h // 2
+                kk = oracle.e4m3_decode(oracle.quantize_e4m3(k[:, g], b.dtype, SCALES[0])) * SCALES[0]
+                vv = oracle.e4m3_decode(oracle.quantize_e4m3(v[:, g], b.dtype, SCALES[1])) * SCALES[1]
+                ref = oracle.causal_attention(oracle.to_f64(q[lo:hi, h], b.dtype), kk, vv, b.query_positions(r),
+                                              b.softmax_scale)
+                err = max(err, float(np.max(np.abs(got[lo:hi, h] - ref))))
+        _say(f"pool past 4 GiB ({path}): max abs err {err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= TOL
+    del gb
+    torch.cuda.empty_cache()
