@@ -281,7 +281,7 @@ pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, in
  * o must not alias q.  Run the pensieve_kv_append of this step's rows first,
  * on the same stream.
  * A request whose work items would run much longer than the batch's fair
- * share (total KV blocks over all items / 1024, at least 64 blocks) is cut
+ * share (total KV blocks over all items / 512, at least 64 blocks) is cut
  * into P partitions of its blocks (split-KV, as in the PersistentKV paper,
  * section 2); its partials go to the workspace and a final merge kernel
  * combines them into o.  Short batches are never split.

@@ -64,10 +64,11 @@ constexpr int kMatrixMinGroup = 4;
 constexpr int kMfmaRows = 128;       // query vectors per matrix-core item
 constexpr int kMaxPartitions = 256;
 // Adaptive split-KV of pensieve_attn_fwd: the plan aims at about kSplitTargetItems work
-// items of similar length (four workgroups per CU of MI355X's 256); a request whose one
-// item would be longer than that share is cut into partitions of at least kSplitMinBlocks
-// blocks (and at least one 64-key tile).
-constexpr long long kSplitTargetItems = 1024;
+// items of similar length -- one round of the matrix-core kernel, two workgroups on each of
+// MI355X's 256 CUs, so that the long requests' items all run at once instead of leaving a
+// partial second round; a request whose one item would be longer than that share is cut into
+// partitions of at least kSplitMinBlocks blocks (and at least one 64-key tile).
+constexpr long long kSplitTargetItems = 512;
 constexpr long long kSplitMinBlocks = 64;
 constexpr size_t kAlign = 256;
 

@@ -61,7 +61,7 @@ ADAPTIVE = {
     "long_prefill_gqa_bf16": lambda: custom_batch([6000, 9000, 200], [300, 1, 5], num_heads=8, num_kv_heads=2,
                                                   head_dim=128, dtype="bf16", seed=62),
     # partially evicted history recomputed ahead of new rows, d = 64
-    "recompute_d64_f16": lambda: custom_batch([5000, 40], [64, 3], [1504, 0], num_heads=4, num_kv_heads=4,
+    "recompute_d64_f16": lambda: custom_batch([5000, 40], [64, 3], [752, 0], num_heads=4, num_kv_heads=4,
                                               head_dim=64, dtype="f16", seed=63),
 }
 
