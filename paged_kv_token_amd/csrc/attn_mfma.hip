@@ -222,7 +222,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   const float slack_raw = kSlack / c;
 
   // ---- this lane's query row --------------------------------------------------------------
-  const int tok = w * TOKW + n / G;
+  // Row block of this wave, rotated by the workgroup index: in items with fewer than 128 query
+  // vectors the busy waves then fall on different SIMDs in the two workgroups sharing a CU.
+  const int wr = (w + (int)(blockIdx.x & 3)) & 3;
+  const int tok = wr * TOKW + n / G;
   const bool row_valid = tok < it.q_count;
   const size_t qrow = (size_t)row0 + it.q_begin + (row_valid ? tok : 0);
   const int h = g * G + (n % G);
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   f32x16 s_cur[2], s_nxt[2];
   // A wave whose 32 query vectors all lie past the item's rows (short prefill items) still
   // loads its share of every tile and meets every barrier, but computes nothing.
-  const bool wave_idle = uniform(w * TOKW >= it.q_count ? 1 : 0) != 0;
+  const bool wave_idle = uniform(wr * TOKW >= it.q_count ? 1 : 0) != 0;
   wait_vmem_all();                           // query rows and positions have landed
   if (ntiles > 0) {
     issue(a.k_pool, koff, 0, kstage(0));
@@ -477,7 +480,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
   __syncthreads();                            // every wave is done reading the pipeline stages
   {
-    uint8_t* orow = lds + (w * 32 + n) * OROW;
+    uint8_t* orow = lds + (wr * 32 + n) * OROW;
 #pragma unroll
     for (int j = 0; j < MBD; ++j)
 #pragma unroll
