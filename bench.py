@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -463,6 +464,63 @@ def fp8_measure(index: int, steps: int, warmup: int, full_step: bool):
     return out
 
 
+def split_sweep(steps: int = 20, warmup: int = 3):
+    """Split-KV crossover on long-context decode batches: the adaptive plan of pensieve_attn_fwd
+    against never splitting and against a fixed 32-way split, as the number of long requests
+    grows (timing only: pools hold device-side random values, 40/40 heads, d = 128, bf16)."""
+    import torch
+    H, heads, d = 32768, 40, 128
+    cases = [(r, 0) for r in (1, 2, 4, 8, 16, 32)] + [(8, 24)]    # (long requests, short ones)
+    rows = []
+    for n_long, n_short in cases:
+        ctx = np.array([H + 1] * n_long + [1024 + 1] * n_short, dtype=np.int32)
+        R = len(ctx)
+        cu = np.arange(R + 1, dtype=np.int32)
+        nblk = -(-ctx // 16)
+        NB = int(nblk.sum())
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        perm = torch.randperm(NB, device="cuda", generator=gen).to(torch.int32)
+        stride = int(nblk.max())
+        bt = torch.zeros((R, stride), dtype=torch.int32, device="cuda")
+        off = 0
+        for r in range(R):
+            bt[r, :nblk[r]] = perm[off:off + nblk[r]]
+            off += int(nblk[r])
+        kp = torch.randn((NB, heads, 16, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        vp = torch.randn((NB, heads, d, 16), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        q = torch.randn((R, heads, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        o = torch.empty_like(q)
+        ctx_d, cu_d = torch.from_numpy(ctx).cuda(), torch.from_numpy(cu).cuda()
+        mk = lambda flags: pk.make_desc(num_heads=heads, num_kv_heads=heads, head_dim=d, num_blocks=NB,
+                                        block_table_stride=stride, dtype=pk.PENSIEVE_BF16,
+                                        softmax_scale=1 / math.sqrt(d), context_lens_host=ctx, cu_q_lens_host=cu,
+                                        flags=flags)
+        d_ad, d_ns = mk(0), mk(pk.PENSIEVE_FLAG_NO_SPLIT)
+        ws_bytes = max(pk.pensieve_attn_workspace_size(d_ad), pk.pensieve_attn_workspace_size(d_ad, 32), 256)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        po = torch.empty((R, heads, 32, d), dtype=torch.float32, device="cuda")
+        pm = torch.empty((R, heads, 32), dtype=torch.float32, device="cuda")
+        pl = torch.empty((R, heads, 32), dtype=torch.float32, device="cuda")
+        plan = pk.pensieve_debug_plan(d_ad)
+        parts = sorted({int(x[6]) for x in plan if x[4] > 0})
+
+        def fixed32():
+            pk.pensieve_attn_split_partial(d_ad, 32, q, kp, vp, bt, ctx_d, cu_d, None, po, pm, pl, ws)
+            pk.pensieve_attn_split_merge(po, pm, pl, o)
+        t_ad, _ = time_steps(lambda: pk.pensieve_attn_fwd(d_ad, q, kp, vp, bt, ctx_d, cu_d, None, o, ws), steps, warmup)
+        t_ns, _ = time_steps(lambda: pk.pensieve_attn_fwd(d_ns, q, kp, vp, bt, ctx_d, cu_d, None, o, ws), steps, warmup)
+        t_32, _ = time_steps(fixed32, steps, warmup)
+        kv = 2 * int(ctx.sum()) * heads * d * 2
+        row = {"long_requests": n_long, "short_requests": n_short, "adaptive_partitions": parts,
+               "adaptive_ms": round(t_ad, 4), "no_split_ms": round(t_ns, 4), "split32_ms": round(t_32, 4),
+               "adaptive_hbm_frac": round(kv / (t_ad * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(json.dumps(row))
+        rows.append(row)
+        del kp, vp, q, o, ws, po, pm, pl, bt
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -476,6 +534,8 @@ def main():
     ap.add_argument("--no-hbm-copy", action="store_true", help="skip the device-copy bandwidth measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (a reference kernel for HBM counters)")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="only measure the split-KV crossover on long-context decode batches and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path needs no collective); --gpus {args.gpus} is not run.",
@@ -486,6 +546,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pk.load_library()
+    if args.split_sweep:
+        print(json.dumps({"split_sweep": split_sweep()}), flush=True)
+        return
     counters = load_counters()
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20

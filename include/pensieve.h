@@ -94,6 +94,9 @@ typedef enum pensieve_dtype {
  * groups of 4 or more).  Results agree within the stated tolerances either
  * way. */
 #define PENSIEVE_FLAG_VECTOR_ONLY 1
+/* pensieve_batch_desc.flags: pensieve_attn_fwd keeps every request whole (no
+ * adaptive split-KV; no partials, no merge). */
+#define PENSIEVE_FLAG_NO_SPLIT 2
 
 /* Shape of one unified batch plus host copies of its lengths (used to
  * validate and to plan the work; the device copies passed to the compute
@@ -108,7 +111,7 @@ typedef struct pensieve_batch_desc {
   int32_t block_table_stride;   /* int32 entries per block-table row */
   int32_t dtype;                /* pensieve_dtype of Q and O (F32, F16, BF16) */
   float softmax_scale;          /* scale on q.k before the softmax, e.g. 1/sqrt(head_dim); > 0 */
-  int32_t flags;                /* 0, or PENSIEVE_FLAG_VECTOR_ONLY */
+  int32_t flags;                /* 0, or PENSIEVE_FLAG_VECTOR_ONLY | PENSIEVE_FLAG_NO_SPLIT */
   const int32_t* context_lens_host;  /* [num_reqs] */
   const int32_t* cu_q_lens_host;     /* [num_reqs + 1], cu_q_lens_host[0] == 0 */
   int32_t kv_dtype;             /* element type of both pools: dtype itself, or

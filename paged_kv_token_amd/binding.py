@@ -25,6 +25,7 @@ PENSIEVE_ERR_WORKSPACE_TOO_SMALL = 3
 PENSIEVE_ERR_HIP = 4
 PENSIEVE_F32, PENSIEVE_F16, PENSIEVE_BF16, PENSIEVE_FP8_E4M3 = 0, 1, 2, 3
 PENSIEVE_FLAG_VECTOR_ONLY = 1
+PENSIEVE_FLAG_NO_SPLIT = 2
 
 EXPORTED = (
     "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",

@@ -111,7 +111,8 @@ pensieve_status check_desc(const pensieve_batch_desc* d) {
   if (d->num_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_blocks must be > 0");
   if (d->block_table_stride <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "block_table_stride must be > 0");
   if (!(d->softmax_scale > 0.f)) return fail(PENSIEVE_ERR_INVALID_ARG, "softmax_scale must be > 0");
-  if (d->flags & ~PENSIEVE_FLAG_VECTOR_ONLY) return fail(PENSIEVE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(PENSIEVE_FLAG_VECTOR_ONLY | PENSIEVE_FLAG_NO_SPLIT))
+    return fail(PENSIEVE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
   if (d->num_reqs > 0 && (!d->context_lens_host || !d->cu_q_lens_host))
     return fail(PENSIEVE_ERR_INVALID_ARG, "context_lens_host / cu_q_lens_host is NULL");
   if (d->num_reqs > 0 && d->cu_q_lens_host[0] != 0) return fail(PENSIEVE_ERR_INVALID_ARG, "cu_q_lens_host[0] != 0");
@@ -242,7 +243,7 @@ long long items_per_kv_head(int q, int G, bool use_matrix) {
 // kSplitTargetItems, and a request is cut only when its items are longer than the share.
 std::vector<int> choose_partitions(const pensieve_batch_desc* d, int num_partitions) {
   std::vector<int> P(d->num_reqs, num_partitions >= 1 ? num_partitions : 1);
-  if (num_partitions >= 1) return P;
+  if (num_partitions >= 1 || (d->flags & PENSIEVE_FLAG_NO_SPLIT)) return P;
   const int G = d->num_heads / d->num_kv_heads;
   const bool mat = matrix_ok(d);
   long long total = 0;

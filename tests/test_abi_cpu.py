@@ -276,3 +276,13 @@ def test_fp8_append_rejects_bad_arguments(lib, args, status):
     st = lib.pensieve_kv_append_fp8(None, None, None, None, None, a["n"], 2, a["d"], 16, 10, a["src"], a["ks"],
                                     a["vs"], None)
     assert st == status
+
+
+def test_no_split_flag_keeps_every_request_whole(lib):
+    b = custom_batch([20000, 300, 300], [1, 1, 40], num_heads=8, num_kv_heads=8, head_dim=128, dtype="f16", seed=5)
+    split = pk.pensieve_debug_plan(desc_for(b))
+    whole = pk.pensieve_debug_plan(desc_for(b, flags=pk.PENSIEVE_FLAG_NO_SPLIT))
+    assert split[split[:, 4] > 0][:, 6].max() > 1
+    assert np.all(whole[:, 6] == 1)
+    assert (pk.pensieve_attn_workspace_size(desc_for(b, flags=pk.PENSIEVE_FLAG_NO_SPLIT))
+            < pk.pensieve_attn_workspace_size(desc_for(b)))

@@ -84,3 +84,13 @@ def test_adaptive_split_in_attn_fwd(name, path):
     err = float(np.max(np.abs(got - ref)))
     _say(f"adaptive {name}/{path}: max abs err {err:.3e}")
     assert err <= 1e-2
+
+
+def test_no_split_flag_matches_the_oracle():
+    b = ADAPTIVE["long_decode_among_short_f16"]()
+    gb = upload(b)
+    ref = oracle_output(b)
+    got = to_f64(run_attn(gb, pk.PENSIEVE_FLAG_NO_SPLIT))
+    err = float(np.max(np.abs(got - ref)))
+    _say(f"no-split flag: max abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= 1e-2
