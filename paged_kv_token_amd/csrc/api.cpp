@@ -411,10 +411,15 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   if (!st) return e;
   std::lock_guard<std::mutex> lk(st->mu);
   if (!st->slab) {
-    if ((e = hipHostMalloc(&st->slab, Stager::kSlots * Stager::kSlotBytes, hipHostMallocMapped)) != hipSuccess)
-      return e;
+    void* slab = nullptr;
     void* slab_mapped = nullptr;
-    if ((e = hipHostGetDevicePointer(&slab_mapped, st->slab, 0)) != hipSuccess) return e;
+    if ((e = hipHostMalloc(&slab, Stager::kSlots * Stager::kSlotBytes, hipHostMallocMapped)) != hipSuccess)
+      return e;
+    if ((e = hipHostGetDevicePointer(&slab_mapped, slab, 0)) != hipSuccess) {
+      (void)hipHostFree(slab);
+      return e;
+    }
+    st->slab = slab;
     for (int i = 0; i < Stager::kSlots; ++i) {
       st->slots[i].host = static_cast<uint8_t*>(st->slab) + i * Stager::kSlotBytes;
       st->slots[i].mapped = static_cast<uint8_t*>(slab_mapped) + i * Stager::kSlotBytes;
@@ -430,6 +435,8 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   if (s.cap < bytes) {
     if (s.owned && (e = hipHostFree(s.host)) != hipSuccess) return e;
     s.host = nullptr;
+    s.mapped = nullptr;
+    s.cap = 0;            // stays empty if the allocation below fails
     s.owned = false;
     size_t cap = 2 * Stager::kSlotBytes;
     while (cap < bytes) cap *= 2;
