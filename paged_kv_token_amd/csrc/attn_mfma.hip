@@ -8,8 +8,10 @@
 // request x the G query heads sharing KV head g, over one partition of the
 // request's KV blocks.  Four waves each own 32 query vectors (row-major over
 // (token, head)).  KV is streamed in 64-token tiles (four 16-token blocks
-// found through the block table): every thread loads its share of the tile
-// into registers while the waves compute on the previous tile from LDS.
+// found through the block table), each wave loading one block of every tile
+// straight into LDS one step ahead of its use, with one workgroup barrier per
+// tile.  Pools may hold f16 / bf16 or E4M3 codes (widened exactly on the way
+// from LDS to the MFMA operands).
 //
 // Per wave and tile, with v_mfma_f32_32x32x16_{f16,bf16}:
 //   S^T (64 keys x 32 rows)  = K_tile . Q^T        (2 x D/16 MFMAs)
@@ -374,14 +376,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     uint8_t* const v_free = lds + (3 - PAR) * STAGE;     // V stage of tile ti - 1
     const int t0 = t_begin + ti * KT;
     const bool k2 = ti + 2 < ntiles, v1 = ti + 1 < ntiles;
+    // The only loads in flight are this wave's K(ti + 1) and V(ti), issued one step ago: wait for
+    // them; then one barrier makes every wave's loads visible and frees the stages of K(ti) (QK(ti)
+    // is done) and V(ti - 1) (PV(ti - 1) is done) for the next loads.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
     __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
-    lds_barrier();                            // every wave is done with QK(ti) and PV(ti - 1)
+    lds_barrier();
     if (k2) issue(a.k_pool, koff, ti + 2, k_free);
     if (v1) issue(a.v_pool, voff, ti + 1, v_free);
-    if (k2) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
-    else if (v1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-    lds_barrier();                            // K(ti + 1) and V(ti) are in LDS
     if (t0 + KT > t_valid) {
       // Tail: keys at or past t_valid must contribute exactly 0; stale V may hold NaN.
 #pragma unroll
