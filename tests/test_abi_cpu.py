@@ -286,3 +286,24 @@ def test_no_split_flag_keeps_every_request_whole(lib):
     assert np.all(whole[:, 6] == 1)
     assert (pk.pensieve_attn_workspace_size(desc_for(b, flags=pk.PENSIEVE_FLAG_NO_SPLIT))
             < pk.pensieve_attn_workspace_size(desc_for(b)))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_covers_random_batches(lib, seed):
+    """Random ragged batches (empty requests, first turns, long contexts, every head grouping,
+    both kernels, adaptive and fixed splits): every (row, head, partition) is planned once."""
+    rng = np.random.default_rng(500 + seed)
+    R = int(rng.integers(1, 24))
+    hist = rng.integers(0, 20000 if seed % 3 == 0 else 2000, size=R)
+    new = np.where(rng.random(R) < 0.2, 0, rng.integers(1, 300, size=R))
+    hist = np.where((new == 0) & (hist == 0), 1, hist)
+    hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    b = custom_batch(hist, new, num_heads=hkv * G, num_kv_heads=hkv, head_dim=int(rng.choice([64, 128])),
+                     dtype=str(rng.choice(["f16", "bf16", "f32"])), seed=seed)
+    for flags in (0, pk.PENSIEVE_FLAG_VECTOR_ONLY, pk.PENSIEVE_FLAG_NO_SPLIT):
+        seen, want = _coverage(b, pk.pensieve_debug_plan(desc_for(b, flags=flags)))
+        assert np.array_equal(seen, want), flags
+    for P in (3, 32):
+        seen, want = _coverage(b, pk.pensieve_debug_plan(desc_for(b), P), P)
+        assert np.array_equal(seen, want), P
