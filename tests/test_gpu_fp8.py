@@ -209,3 +209,34 @@ def test_fp8_pool_offsets_beyond_4_gib():
         assert np.all(np.isfinite(got)) and err <= TOL
     del gb
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_full_size_fp8_sampled_parity(index):
+    """The workloads the benchmark times with E4M3 pools, at full size: sampled (request, head)
+    outputs against the oracle over each request's quantised logical K/V."""
+    scales = (1 / 128, 1 / 128)
+    b = config_batch(index)
+    _say(f"full-size {b.name}: R={b.num_reqs} T={b.total_q}")
+    gb = upload(b, kv_fp8=scales)
+    got = to_f64(run_attn(gb))
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(300 + index)
+    reqs = sorted(set(rng.choice(b.num_reqs, size=3, replace=False).tolist() + [int(np.argmax(b.context_lens))]))
+    heads = sorted(set([0, b.num_heads - 1] + rng.choice(b.num_heads, size=2, replace=False).tolist()))
+    G = b.num_heads // b.num_kv_heads
+    q = b.q_all()
+    worst = 0.0
+    for r in reqs:
+        k, v = b.request_kv(r)
+        lo, hi = int(b.cu_q_lens[r]), int(b.cu_q_lens[r + 1])
+        for h in heads:
+            g = h // G
+            kk = oracle.e4m3_decode(oracle.quantize_e4m3(k[:, g], b.dtype, scales[0])) * scales[0]
+            vv = oracle.e4m3_decode(oracle.quantize_e4m3(v[:, g], b.dtype, scales[1])) * scales[1]
+            ref = oracle.causal_attention(oracle.to_f64(q[lo:hi, h], b.dtype), kk, vv, b.query_positions(r),
+                                          b.softmax_scale)
+            worst = max(worst, float(np.max(np.abs(got[lo:hi, h] - ref))))
+    _say(f"full-size {b.name}: requests {reqs} heads {heads}: max abs err {worst:.3e}")
+    assert worst <= TOL
+    del gb
