@@ -75,3 +75,36 @@ def test_custom_batch_slots_follow_block_table():
         slots = b.slots_for(r, pos)
         assert np.array_equal(slots // 16, b.block_tables[r][pos // 16])
         assert np.array_equal(slots % 16, pos % 16)
+
+
+def test_conversation_script_turns():
+    """Each conversation alternates idle spells and turns: a prompt step (16-96 tokens) followed by
+    2-6 decode steps of one token (cut at the end of the run); the draws are seeded."""
+    from workloads import conversation_script
+    s = conversation_script(7, 9, 60)
+    assert s.shape == (60, 9) and s.dtype == np.int32
+    assert np.array_equal(s, conversation_script(7, 9, 60))
+    assert not np.array_equal(s, conversation_script(8, 9, 60))
+    for c in range(9):
+        col = s[:, c]
+        t = 0
+        while t < 60:
+            if col[t] == 0:
+                t += 1
+                continue
+            assert 16 <= col[t] <= 96, (c, t, col[t])      # a turn opens with its prompt
+            t += 1
+            n = 0
+            while t < 60 and col[t] == 1:
+                n += 1
+                t += 1
+            assert n <= 6 and (n >= 2 or t == 60), (c, t, n)
+
+
+def test_draw_rows_is_seeded_and_rounded():
+    from workloads import draw_rows
+    a = draw_rows((1, 2, 3), (5, 4), "bf16")
+    assert a.dtype == np.uint16 and a.shape == (5, 4)
+    assert np.array_equal(a, draw_rows((1, 2, 3), (5, 4), "bf16"))
+    f = draw_rows((1, 2, 3), (5, 4), "f32")
+    assert np.array_equal(bf16_bits_from_f32(f), a)     # same normals, rounded to bf16
