@@ -287,7 +287,8 @@ pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, in
  * share (total KV blocks over all items / 512, at least 64 blocks) is cut
  * into P partitions of its blocks (split-KV, as in the PersistentKV paper,
  * section 2); its partials go to the workspace and a final merge kernel
- * combines them into o.  Short batches are never split.
+ * combines them into o.  Short batches are never split, and no request is
+ * when desc->flags has PENSIEVE_FLAG_NO_SPLIT.
  */
 pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q, const void* k_pool,
                                   const void* v_pool, const int32_t* block_tables,
