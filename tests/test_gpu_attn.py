@@ -42,6 +42,8 @@ CASES = {
                                                    head_dim=64, dtype="bf16", seed=22),
     "gqa16_f16": lambda: custom_batch([40, 200], [20, 3], num_heads=16, num_kv_heads=1, head_dim=128,
                                       dtype="f16", seed=23),
+    "gqa32_d64_bf16": lambda: custom_batch([0, 70, 300], [5, 1, 33], num_heads=32, num_kv_heads=1, head_dim=64,
+                                           dtype="bf16", seed=26),
     "gqa8_decode_bf16": lambda: custom_batch([0, 1, 15, 16, 63, 64, 65, 700, 1999], [1] * 9, num_heads=16,
                                              num_kv_heads=2, head_dim=128, dtype="bf16", seed=25),
     "f32_d128_gqa2": lambda: custom_batch([30, 0, 77], [3, 40, 1], num_heads=4, num_kv_heads=2, head_dim=128,

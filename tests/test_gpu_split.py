@@ -24,6 +24,9 @@ CASES = {
     "tiny_f32_p4": (lambda: config_batch(0), 4),
     "p1_f16": (lambda: custom_batch([300, 5], [40, 1], num_heads=2, num_kv_heads=2, head_dim=64, dtype="f16",
                                     seed=52), 1),
+    # the largest partition count: 256 partitions of a 5000-token prefill and of short requests
+    "p256_max_bf16": (lambda: custom_batch([4950, 60, 0], [50, 1, 7], num_heads=4, num_kv_heads=2, head_dim=64,
+                                           dtype="bf16", seed=53), 256),
 }
 
 
