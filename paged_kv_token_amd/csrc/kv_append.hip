@@ -5,11 +5,16 @@
 // fixed-size blocks allocated on demand in non-contiguous memory).
 //
 // Pools: K [num_blocks][Hkv][16][D] (token rows), V [num_blocks][Hkv][D][16]
-// (dim rows).  One workgroup copies 16 consecutive new tokens of one KV head:
+// (dim rows).  A run is a stretch of tokens whose slots follow each other
+// inside one block (a request's new tokens fill its blocks in order, usually
+// starting mid-block).  One workgroup serves one KV head and a window of 16
+// consecutive tokens, and writes every run that starts inside the window, to
+// its end (at most 15 tokens past the window).  So the 32-byte dim rows of a
+// block that one run fills are written whole by one workgroup, instead of in
+// two parts by two workgroups that may sit on different XCDs (a partly
+// written sector costs a read-modify-write when it leaves the caches).
 // K rows go straight to their slots with 16-byte stores; V rows are staged in
-// LDS and each run of consecutive slots (a request's new tokens fill its
-// blocks in order, usually starting mid-block) leaves in the widest aligned
-// stores its position allows.
+// LDS and each run leaves in the widest aligned stores its position allows.
 #include "device_common.h"
 #include "launch.h"
 
@@ -41,22 +46,23 @@ __device__ __forceinline__ void store_elems(uint8_t* dst, const uint8_t* src, in
   }
 }
 
-// V rows staged in LDS (16 token rows of D elements of EB bytes) to the dim-major V tiles of
-// their slots.  One thread per dim row walks the 16 tokens run by run -- a run is a stretch
-// of consecutive slots inside one block -- and writes each run with the widest aligned stores
-// (16, 8, 4, 2 or 1 bytes), so a run that starts mid-block still leaves in wide stores.
-template <int EB, int D>
+// V rows staged in LDS (NT token rows of D elements of EB bytes; a negative slot is skipped) to
+// the dim-major V tiles of their slots.  One thread per dim row walks the tokens run by run and
+// writes each run with the widest aligned stores (16, 8, 4, 2 or 1 bytes), so a run that starts
+// mid-block still leaves in wide stores.  (Sharing a dim row's runs among several threads
+// measured slower.)
+template <int EB, int D, int NT>
 __device__ __forceinline__ void store_v_runs(const int* s_slot, const uint8_t* s_v, uint8_t* v_pool,
                                              int num_kv_heads, int g, int tid) {
   constexpr size_t TILE = (size_t)16 * D * EB;
   constexpr int ROW = D * EB;
   for (int d = tid; d < D; d += 256) {
     int t = 0;
-    while (t < 16) {
+    while (t < NT) {
       const int s = s_slot[t];
       if (s < 0) { ++t; continue; }
       int n = 1;
-      while (t + n < 16 && s_slot[t + n] == s + n && ((s + n) & 15) != 0) ++n;
+      while (t + n < NT && s_slot[t + n] == s + n && ((s + n) & 15) != 0) ++n;
       uint8_t* row = v_pool + ((size_t)(s >> 4) * num_kv_heads + g) * TILE + (size_t)d * 16 * EB;
       int p = s & 15;
       const int end = p + n;
@@ -83,17 +89,37 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
                                                         int num_kv_heads) {
   constexpr int ROW = D * EB;        // bytes of one token's row for one head
   constexpr int CPR = ROW / 16;      // 16-byte chunks per row
-  __shared__ int s_slot[16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[16 * ROW];
+  constexpr int NT = 32;             // tokens t0 .. t0 + 31: the window and the 15 tokens after it
+  __shared__ int s_raw[NT + 1];      // slots of tokens t0 - 1 .. t0 + 31 (-1 outside the batch)
+  __shared__ int s_slot[NT];         // slots of the tokens this workgroup writes, else -1
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[NT * ROW];
 
   const int t0 = blockIdx.x * 16;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
-  if (tid < 16) s_slot[tid] = (t0 + tid < num_tokens) ? slots[t0 + tid] : -1;
+  if (tid < NT + 1) {
+    const int i = t0 - 1 + tid;
+    s_raw[tid] = (i >= 0 && i < num_tokens) ? slots[i] : -1;
+  }
+  __syncthreads();
+  if (tid < NT) {
+    // Token t0 + j continues its predecessor's run when its slot is the next one in the same
+    // block.  It is ours when its run starts inside the window: for j < 16, unless every token
+    // from t0 to it continues a run that began before t0; for j >= 16, when every token from
+    // t0 + 16 to it continues (a run spans at most 16 tokens, so it then began at t0 + 1 or later).
+    auto cont = [&](int j) {
+      const int s = s_raw[j + 1], prev = s_raw[j];
+      return s >= 0 && prev >= 0 && s == prev + 1 && (s & 15) != 0;
+    };
+    bool chain = true;
+    for (int j = (tid < 16 ? 0 : 16); j <= tid; ++j) chain = chain && cont(j);
+    const bool ours = tid < 16 ? !chain : chain;
+    s_slot[tid] = ours ? s_raw[tid + 1] : -1;
+  }
   __syncthreads();
 
   const size_t tile_bytes = (size_t)16 * ROW;
-  for (int c = tid; c < 16 * CPR; c += 256) {
+  for (int c = tid; c < NT * CPR; c += 256) {
     const int tok = c / CPR, wc = c % CPR;
     const int s = s_slot[tok];
     if (s >= 0) {
@@ -106,7 +132,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
   }
   __syncthreads();
 
-  store_v_runs<EB, D>(s_slot, s_v, v_pool, num_kv_heads, g, tid);
+  store_v_runs<EB, D, NT>(s_slot, s_v, v_pool, num_kv_heads, g, tid);
 }
 
 template <int EB, int D>

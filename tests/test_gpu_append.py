@@ -100,3 +100,60 @@ def test_append_full_size_sampled_blocks(index):
             gv = to_host_storage(gb.v_pool[phys:phys + 1], b.dtype)
             assert np.array_equal(_bits(gk), _bits(mk)), (r, j)
             assert np.array_equal(_bits(gv), _bits(mv)), (r, j)
+
+
+def _run_slots(rng, nb: int) -> np.ndarray:
+    """In-order runs starting at every block offset, of lengths that end inside, at and past the
+    16-token windows of the append grid; a block whose two halves arrive far apart in the token
+    list; skipped tokens inside runs; a token count that is not a multiple of 16."""
+    blocks = iter(rng.permutation(nb).tolist())
+    slots = []
+    for start in range(16):
+        for length in (1, 15 - start if start < 15 else 2, 16, 17, 31, 33):
+            s = next(blocks) * 16 + start
+            for k in range(max(length, 1)):
+                if k > 0 and s % 16 == 0:
+                    s = next(blocks) * 16
+                slots.append(s)
+                s += 1
+    split = next(blocks) * 16
+    slots[5:5] = list(range(split, split + 8))
+    slots.extend(range(split + 8, split + 16))
+    slots = np.asarray(slots, dtype=np.int32)
+    slots[rng.choice(len(slots), 25, replace=False)] = -1
+    return slots[:len(slots) - 3]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_append_runs_across_windows(dtype):
+    """Runs that start anywhere in a block and cross the append grid's 16-token windows are
+    written exactly once: whole pools equal the oracle's append bit for bit."""
+    import torch
+    import paged_kv_token_amd as pk
+    from gpu_harness import poison_, to_device, torch_dtype
+    rng = np.random.default_rng(23)
+    nb, hkv, d = 420, 2, 128 if dtype != "f32" else 64
+    slots = _run_slots(rng, nb)
+    n = len(slots)
+    assert n % 16 != 0
+    sd = storage_dtype(dtype)
+    x = rng.standard_normal((2, n, hkv, d)).astype(np.float32)
+    if dtype == "f32":
+        k_new, v_new = x[0], x[1]
+    elif dtype == "f16":
+        k_new, v_new = x[0].astype(np.float16), x[1].astype(np.float16)
+    else:
+        from workloads import bf16_bits_from_f32
+        k_new, v_new = bf16_bits_from_f32(x[0]), bf16_bits_from_f32(x[1])
+    fill = poison_fill(dtype)
+    k_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
+    v_ref = np.full((nb, hkv, d, 16), fill, dtype=sd)
+    oracle.append_kv(k_ref, v_ref, k_new, v_new, slots, 16)
+    _say(f"runs {dtype}: n={n} nb={nb}")
+    k_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    v_pool = poison_(torch.empty((nb, hkv, d, 16), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    pk.pensieve_kv_append(to_device(k_new, dtype), to_device(v_new, dtype), k_pool, v_pool,
+                          torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(to_host_storage(k_pool, dtype)), _bits(k_ref))
+    assert np.array_equal(_bits(to_host_storage(v_pool, dtype)), _bits(v_ref))
