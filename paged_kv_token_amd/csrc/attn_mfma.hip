@@ -466,6 +466,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) acc[j0 + jj] = MM::mma(vop[jj][ks], pb[ks], acc[j0 + jj]);
     }
+    // Issue order for the region above: each MFMA followed by three VALU instructions, so the
+    // exponentials of this tile run while the QK MFMAs of the next one execute, and the weight
+    // conversions and row sums while the PV MFMAs do.  Left to itself the scheduler issues the QK
+    // MFMAs back to back, each behind its own LDS operand reads.  E4M3 tiles keep the
+    // scheduler's order: their operand widening adds four VALU conversions per MFMA, and the
+    // same pattern made them slower.
+    if constexpr (!F8) {
+#pragma unroll
+      for (int i = 0; i < 2 * KS + 4 * MBD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU instructions
+      }
+    }
   };
 
   using P0 = std::integral_constant<int, 0>;
