@@ -103,7 +103,8 @@ class DeviceBatch:
         self.desc = pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                                  num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
                                  dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
-                                 context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens, **fp8)
+                                 context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens,
+                                 q_pos_host=None if b.has_default_positions else b.q_pos, **fp8)
         self.ws = torch.empty(max(pk.pensieve_attn_workspace_size(self.desc), 256), dtype=torch.uint8, device="cuda")
         self.sets = [(self.k_pool, self.v_pool, self.q, self.o)]
         for _ in range(copies - 1):

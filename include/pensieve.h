@@ -118,6 +118,13 @@ typedef struct pensieve_batch_desc {
                                    PENSIEVE_FP8_E4M3 when dtype is F16 or BF16 */
   float k_scale, v_scale;       /* FP8_E4M3 pools: value = code * scale (finite, > 0);
                                    ignored for other pools */
+  const int32_t* q_pos_host;    /* [total_q] host copy of the q_pos array passed to the
+                                   attention calls, or NULL.  Read only to plan: each
+                                   matrix-core work item is costed by the keys its rows can
+                                   see, and the items are spread over the XCDs by that cost.
+                                   When NULL while q_pos is given, an item is costed by its
+                                   request's whole context.  It never changes a result; values
+                                   that differ from q_pos only change the work balance. */
 } pensieve_batch_desc;
 
 /* Library version string, e.g. "pensieve 0.1 gfx950". */
@@ -271,6 +278,9 @@ pensieve_status pensieve_cache_build_batch(const pensieve_conversation* conversa
  * (about rows x Hq x P x (head_dim + 2) x 4 bytes for the split requests'
  * rows only); it is plain device memory owned by the caller, needs no
  * initialisation and may be reused by the next call on the same stream.
+ * The size depends on every field of the descriptor (q_pos_host included:
+ * it changes how the work list is laid out), so size the workspace with the
+ * descriptor the attention call receives.
  */
 pensieve_status pensieve_attn_workspace_size(const pensieve_batch_desc* desc, int32_t num_partitions,
                                              size_t* bytes);

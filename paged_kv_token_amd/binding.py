@@ -61,6 +61,7 @@ class BatchDesc(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("q_pos_host", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -162,7 +163,7 @@ def _stream(stream):
 def make_desc(*, num_heads: int, num_kv_heads: int, head_dim: int, num_blocks: int, block_table_stride: int,
               dtype: int, softmax_scale: float, context_lens_host, cu_q_lens_host, block_size: int = 16,
               flags: int = 0, kv_dtype: Optional[int] = None, k_scale: float = 1.0,
-              v_scale: float = 1.0) -> BatchDesc:
+              v_scale: float = 1.0, q_pos_host=None) -> BatchDesc:
     ctx = np.ascontiguousarray(context_lens_host, dtype=np.int32)
     cu = np.ascontiguousarray(cu_q_lens_host, dtype=np.int32)
     d = BatchDesc(len(ctx), num_heads, num_kv_heads, head_dim, block_size, num_blocks, block_table_stride, dtype,
@@ -172,7 +173,13 @@ def make_desc(*, num_heads: int, num_kv_heads: int, head_dim: int, num_blocks: i
     d.kv_dtype = dtype if kv_dtype is None else int(kv_dtype)
     d.k_scale = float(k_scale)
     d.v_scale = float(v_scale)
-    d._keep = (ctx, cu)  # host arrays must outlive the descriptor
+    qp = None
+    if q_pos_host is not None:
+        qp = np.ascontiguousarray(q_pos_host, dtype=np.int32)
+        if qp.shape != (int(cu[-1]) if len(cu) else 0,):
+            raise ValueError("q_pos_host must hold one position per query row")
+        d.q_pos_host = qp.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    d._keep = (ctx, cu, qp)  # host arrays must outlive the descriptor
     return d
 
 

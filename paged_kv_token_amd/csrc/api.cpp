@@ -190,7 +190,7 @@ constexpr int kXcds = 8;
 // One (request, KV head, partition) of matrix-core items: items[first, first + count), all of
 // the same cost.
 struct ItemGroup {
-  long long cost;
+  long long cost;   // total over the group's items
   int first, count;
 };
 
@@ -210,9 +210,14 @@ void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGrou
     int x = 0;
     for (int y = 1; y < kXcds; ++y)
       if (load[y] < load[x]) x = y;
-    load[x] += groups[gi].cost * groups[gi].count;
+    load[x] += groups[gi].cost;
     for (int k = 0; k < groups[gi].count; ++k) bins[x].push_back(groups[gi].first + k);
   }
+  // Longest items of each XCD first (items of a request differ when its rows sit at very
+  // different positions, e.g. recomputed leading rows), so that the XCD's last round holds its
+  // shortest items.
+  for (auto& bin : bins)
+    std::stable_sort(bin.begin(), bin.end(), [&](int a, int b) { return items[a].cost > items[b].cost; });
   size_t longest = 0;
   for (auto& bin : bins) longest = std::max(longest, bin.size());
   PlannedItem filler = items.front();
@@ -315,14 +320,22 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
       for (int g = 0; g < d->num_kv_heads; ++g) {
         if (use_matrix) {
           const int tok_tile = kMfmaRows / G;
-          groups.push_back({(blocks + 1) * 64, (int)mat_items.size(), 0});
+          groups.push_back({0, (int)mat_items.size(), 0});
           for (int q0 = 0; q0 < q; q0 += tok_tile) {
             PlannedItem p{};
-            p.w = {r, q0, std::min(tok_tile, q - q0), g, 0, G, part, P};
+            const int qc = std::min(tok_tile, q - q0);
+            p.w = {r, q0, qc, g, 0, G, part, P};
             p.kernel = kMatrix;
             p.param = G;
-            p.cost = (blocks + 1) * 64;
+            // An item streams the keys of its partition that its last (largest) position can
+            // see, plus a fixed cost of about one block.
+            const long long last = d->q_pos_host ? (long long)d->q_pos_host[d->cu_q_lens_host[r] + q0 + qc - 1]
+                                                 : (long long)L - q + q0 + qc - 1;
+            const long long seen = std::min(std::max(std::min(last + 1, (long long)L) - part * per * kBlockSize, 0LL),
+                                            blocks * kBlockSize);
+            p.cost = ((seen + kBlockSize - 1) / kBlockSize + 1) * 64;
             mat_items.push_back(p);
+            groups.back().cost += p.cost;
             groups.back().count++;
           }
         } else {

@@ -100,7 +100,7 @@ class GpuBackend:
         desc = pk.make_desc(num_heads=num_heads, num_kv_heads=self.k_pool.shape[1], head_dim=self.k_pool.shape[3],
                             num_blocks=self.num_blocks, block_table_stride=block_tables.shape[1],
                             dtype={"f32": 0, "f16": 1, "bf16": 2}[self.dtype], softmax_scale=scale,
-                            context_lens_host=context_lens, cu_q_lens_host=cu_q_lens, **fp8)
+                            context_lens_host=context_lens, cu_q_lens_host=cu_q_lens, q_pos_host=q_pos, **fp8)
         ws = torch.empty(max(pk.pensieve_attn_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
         ws.fill_(0xFF)
         o = torch.full_like(qt, float("nan"))

@@ -70,7 +70,8 @@ class GpuBatch:
         return pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                             num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
                             dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
-                            context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens, flags=flags, **fp8)
+                            context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens, flags=flags,
+                            q_pos_host=None if self.q_pos is None else b.q_pos, **fp8)
 
 
 def upload(batch: Batch, *, append_new: bool = True, poison: bool = True, pass_q_pos: Optional[bool] = None,

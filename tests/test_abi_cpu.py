@@ -307,3 +307,43 @@ def test_plan_covers_random_batches(lib, seed):
     for P in (3, 32):
         seen, want = _coverage(b, pk.pensieve_debug_plan(desc_for(b), P), P)
         assert np.array_equal(seen, want), P
+
+
+def _bin_spread(b, plan, pos):
+    """max / mean over the 8 XCD bins (slot % 8) of the 64-key tiles the matrix-core items' rows
+    can see, from the positions themselves."""
+    mat = plan[plan[:, 0] == 1]
+    load = np.zeros(8)
+    for i, row in enumerate(mat):
+        r, q0, qc = int(row[1]), int(row[3]), int(row[4])
+        if qc:
+            load[i % 8] += -(-(int(pos[int(b.cu_q_lens[r]) + q0 + qc - 1]) + 1) // 64)
+    return load.max() / load.mean()
+
+
+def test_host_positions_balance_the_xcd_bins(lib):
+    """GQA recompute workload: with the host copy of the query positions every matrix-core item is
+    costed by the keys its rows can see, and the eight XCD bins carry equal causal work within 1 %
+    (costed by whole contexts, the recomputed leading rows make them about 6 % apart)."""
+    b = config_batch(3)
+    with_pos = _bin_spread(b, pk.pensieve_debug_plan(desc_for(b, q_pos_host=b.q_pos)), b.q_pos)
+    without = _bin_spread(b, pk.pensieve_debug_plan(desc_for(b)), b.q_pos)
+    assert with_pos < 1.01 and with_pos < without
+
+
+def test_host_positions_never_change_the_work_covered(lib):
+    """Host positions only order the work: true, zero or arbitrary values plan every (row, head,
+    partition) exactly once, and each XCD bin still runs its longest items first."""
+    b = config_batch(3, num_reqs=12, max_hist=3000)
+    rng = np.random.default_rng(3)
+    junk = rng.integers(-2**31, 2**31 - 1, size=b.total_q, dtype=np.int64).astype(np.int32)
+    for qp in (b.q_pos, np.zeros(b.total_q, np.int32), junk):
+        plan = pk.pensieve_debug_plan(desc_for(b, q_pos_host=qp))
+        seen, want = _coverage(b, plan)
+        assert np.array_equal(seen, want)
+        mat = plan[plan[:, 0] == 1]
+        for x in range(8):
+            costs = [row[7] for row in mat[x::8] if row[4] > 0]
+            assert costs == sorted(costs, reverse=True)
+    with pytest.raises(ValueError):
+        desc_for(b, q_pos_host=b.q_pos[:-1])
