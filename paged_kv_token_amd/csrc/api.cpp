@@ -260,11 +260,24 @@ std::vector<int> choose_partitions(const pensieve_batch_desc* d, int num_partiti
     total += items_per_kv_head(q, G, use_matrix) * d->num_kv_heads * (nblk + 1);
   }
   const long long share = std::max(kSplitMinBlocks, total / kSplitTargetItems);
+  // When the matrix-core items leave CUs free, the vector items run beside them on a second
+  // stream, in whatever workgroup slots are left: vector requests then get twice the items.
+  long long matrix_items = 0;
+  bool any_vector = false;
+  for (int r = 0; r < d->num_reqs; ++r) {
+    const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+    if (q == 0) continue;
+    if (routes_to_matrix(mat, q, G)) matrix_items += items_per_kv_head(q, G, true) * d->num_kv_heads;
+    else any_vector = true;
+  }
+  const bool beside = any_vector && matrix_items > 0 && matrix_items < kSplitTargetItems;
+  const long long vshare = beside ? std::max(kSplitMinBlocks, total / (2 * kSplitTargetItems)) : share;
   for (int r = 0; r < d->num_reqs; ++r) {
     const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
     const long long nblk = (d->context_lens_host[r] + kBlockSize - 1) / kBlockSize;
-    if (q == 0 || nblk + 1 <= share) continue;
-    const long long want = (nblk + 1 + share - 1) / share;
+    const long long sh = (q > 0 && routes_to_matrix(mat, q, G)) ? share : vshare;
+    if (q == 0 || nblk + 1 <= sh) continue;
+    const long long want = (nblk + 1 + sh - 1) / sh;
     P[r] = (int)std::max(1LL, std::min({want, (long long)kMaxPartitions, nblk / 4}));
   }
   return P;

@@ -153,14 +153,15 @@ def test_adaptive_split_leaves_ordinary_batches_whole(lib, index):
 
 
 def test_adaptive_split_cuts_only_the_long_requests(lib):
-    """Long-context batch: the longest histories get the most partitions, at least 64
-    blocks each; a batch of short requests beside one long one splits only the long one."""
+    """Long-context batch: among the requests of one kernel the longest histories get the most
+    partitions, at least 64 blocks each; a batch of short requests beside one long one splits
+    only the long one."""
     b = config_batch(4)
     parts = _adaptive_parts(b)
     nblk = -(-b.context_lens // 16)
     assert all(parts[r] > 1 for r in range(b.num_reqs))
-    order = np.argsort(nblk, kind="stable")
-    assert [parts[int(r)] for r in order] == sorted(parts[int(r)] for r in order)
+    decode = [r for r in np.argsort(nblk, kind="stable") if b.q_lens[r] == 1]   # the vector kernel's
+    assert [parts[int(r)] for r in decode] == sorted(parts[int(r)] for r in decode)
     assert all(nblk[r] / parts[r] >= 4 for r in parts)
     mixed = custom_batch([20000] + [300] * 12, [1] * 13, num_heads=8, num_kv_heads=8, head_dim=128, dtype="f16",
                          seed=9)
@@ -347,3 +348,22 @@ def test_host_positions_never_change_the_work_covered(lib):
             assert costs == sorted(costs, reverse=True)
     with pytest.raises(ValueError):
         desc_for(b, q_pos_host=b.q_pos[:-1])
+
+
+def test_vector_requests_beside_matrix_items_split_finer(lib):
+    """Long-context workload: the 512-row prefill request alone fills fewer than 512 matrix-core
+    items, so the three long decode requests (vector kernel, run beside it) are cut against half
+    the usual share, about twice as many partitions as the prefill request's rule gives."""
+    b = config_batch(4)
+    plan = pk.pensieve_debug_plan(desc_for(b))
+    parts = {int(row[1]): int(row[6]) for row in plan if row[4] > 0}
+    kern = {int(row[1]): int(row[0]) for row in plan if row[4] > 0}
+    nblk = -(-b.context_lens.astype(np.int64) // 16)
+    items = np.where(b.q_lens > 1, -(-b.q_lens // 128), 1)
+    share = max(64, int((items * b.num_kv_heads * (nblk + 1)).sum()) // 512)
+    for r in range(b.num_reqs):
+        usual = -(-(int(nblk[r]) + 1) // share)
+        if kern[r] == 1:
+            assert parts[r] == usual
+        else:
+            assert parts[r] >= 2 * usual - 1 and parts[r] > usual
