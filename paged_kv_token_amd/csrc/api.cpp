@@ -194,17 +194,48 @@ struct ItemGroup {
   int first, count;
 };
 
+// Reorder idx so that cost(i) descends, keeping the given order among equal costs.  Plan costs
+// are multiples of 64 over a range of a few thousand steps, so a counting sort over cost / 64
+// does it in linear time; anything else takes a comparison sort.
+template <class Cost>
+void sort_longest_first(std::vector<int>& idx, Cost cost) {
+  thread_local std::vector<int> start_tl, tmp_tl;
+  std::vector<int>& start = start_tl;
+  std::vector<int>& tmp = tmp_tl;
+  long long top = 0;
+  bool steps = true;
+  for (int i : idx) {
+    const long long c = cost(i);
+    top = std::max(top, c / 64);
+    steps = steps && c >= 0 && c % 64 == 0;
+  }
+  if (!steps || top > 8 * (long long)idx.size() + 4096) {
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return cost(a) > cost(b); });
+    return;
+  }
+  start.assign((size_t)top + 2, 0);   // bucket b = top - cost / 64: the largest cost first
+  for (int i : idx) start[(size_t)(top - cost(i) / 64) + 1]++;
+  for (size_t b = 1; b < start.size(); ++b) start[b] += start[b - 1];
+  tmp.resize(idx.size());
+  for (int i : idx) tmp[start[(size_t)(top - cost(i) / 64)]++] = i;
+  idx.swap(tmp);
+}
+
 void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGroup>& groups,
                std::vector<PlannedItem>& out) {
-  std::vector<int> order(groups.size());
+  thread_local std::vector<int> order_tl;
+  thread_local std::vector<int> bins_tl[kXcds];
+  std::vector<int>& order = order_tl;
+  order.resize(groups.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return groups[a].cost > groups[b].cost; });
+  sort_longest_first(order, [&](int g) { return groups[g].cost; });
   if (items.size() < 2 * kXcds) {
     for (int gi : order)
       out.insert(out.end(), items.begin() + groups[gi].first, items.begin() + groups[gi].first + groups[gi].count);
     return;
   }
-  std::vector<int> bins[kXcds];
+  std::vector<int>* const bins = bins_tl;
+  for (int x = 0; x < kXcds; ++x) bins[x].clear();
   long long load[kXcds] = {};
   for (int gi : order) {
     int x = 0;
@@ -216,10 +247,9 @@ void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGrou
   // Longest items of each XCD first (items of a request differ when its rows sit at very
   // different positions, e.g. recomputed leading rows), so that the XCD's last round holds its
   // shortest items.
-  for (auto& bin : bins)
-    std::stable_sort(bin.begin(), bin.end(), [&](int a, int b) { return items[a].cost > items[b].cost; });
+  for (int x = 0; x < kXcds; ++x) sort_longest_first(bins[x], [&](int i) { return items[i].cost; });
   size_t longest = 0;
-  for (auto& bin : bins) longest = std::max(longest, bin.size());
+  for (int x = 0; x < kXcds; ++x) longest = std::max(longest, bins[x].size());
   PlannedItem filler = items.front();
   filler.w.q_count = 0;
   filler.cost = 0;
