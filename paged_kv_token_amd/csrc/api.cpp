@@ -194,31 +194,37 @@ struct ItemGroup {
   int first, count;
 };
 
-// Reorder idx so that cost(i) descends, keeping the given order among equal costs.  Plan costs
-// are multiples of 64 over a range of a few thousand steps, so a counting sort over cost / 64
-// does it in linear time; anything else takes a comparison sort.
-template <class Cost>
-void sort_longest_first(std::vector<int>& idx, Cost cost) {
+// Reorder idx so that key(i) descends, keeping the given order among equal keys: a counting
+// sort when the keys span a small range (plan costs in blocks, cost classes), else a
+// comparison sort.
+template <class Key>
+void sort_descending(std::vector<int>& idx, Key key) {
   thread_local std::vector<int> start_tl, tmp_tl;
   std::vector<int>& start = start_tl;
   std::vector<int>& tmp = tmp_tl;
   long long top = 0;
-  bool steps = true;
+  bool small = true;
   for (int i : idx) {
-    const long long c = cost(i);
-    top = std::max(top, c / 64);
-    steps = steps && c >= 0 && c % 64 == 0;
+    const long long k = key(i);
+    top = std::max(top, k);
+    small = small && k >= 0;
   }
-  if (!steps || top > 8 * (long long)idx.size() + 4096) {
-    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return cost(a) > cost(b); });
+  if (!small || top > 8 * (long long)idx.size() + 4096) {
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return key(a) > key(b); });
     return;
   }
-  start.assign((size_t)top + 2, 0);   // bucket b = top - cost / 64: the largest cost first
-  for (int i : idx) start[(size_t)(top - cost(i) / 64) + 1]++;
+  start.assign((size_t)top + 2, 0);   // bucket b = top - key: the largest key first
+  for (int i : idx) start[(size_t)(top - key(i)) + 1]++;
   for (size_t b = 1; b < start.size(); ++b) start[b] += start[b - 1];
   tmp.resize(idx.size());
-  for (int i : idx) tmp[start[(size_t)(top - cost(i) / 64)]++] = i;
+  for (int i : idx) tmp[start[(size_t)(top - key(i))]++] = i;
   idx.swap(tmp);
+}
+
+// Cost class of a work item: the octave of its length in 64-unit steps, floor(log2(cost / 64)).
+int cost_class(long long cost) {
+  const unsigned long long steps = (unsigned long long)std::max(1LL, cost / 64);
+  return 63 - __builtin_clzll(steps);
 }
 
 void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGroup>& groups,
@@ -228,7 +234,7 @@ void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGrou
   std::vector<int>& order = order_tl;
   order.resize(groups.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
-  sort_longest_first(order, [&](int g) { return groups[g].cost; });
+  sort_descending(order, [&](int g) { return groups[g].cost / 64; });
   if (items.size() < 2 * kXcds) {
     for (int gi : order)
       out.insert(out.end(), items.begin() + groups[gi].first, items.begin() + groups[gi].first + groups[gi].count);
@@ -244,10 +250,13 @@ void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGrou
     load[x] += groups[gi].cost;
     for (int k = 0; k < groups[gi].count; ++k) bins[x].push_back(groups[gi].first + k);
   }
-  // Longest items of each XCD first (items of a request differ when its rows sit at very
-  // different positions, e.g. recomputed leading rows), so that the XCD's last round holds its
-  // shortest items.
-  for (int x = 0; x < kXcds; ++x) sort_longest_first(bins[x], [&](int i) { return items[i].cost; });
+  // Each XCD runs its items by cost class, longest octave first (items of a request differ when
+  // its rows sit at very different positions, e.g. recomputed leading rows), so that its last
+  // round holds its shortest items.  Inside a class the items keep the order above, a request's
+  // items next to each other, so that they run close together in time and share its K/V in the
+  // XCD's L2.
+  for (int x = 0; x < kXcds; ++x)
+    sort_descending(bins[x], [&](int i) { return (long long)cost_class(items[i].cost); });
   size_t longest = 0;
   for (int x = 0; x < kXcds; ++x) longest = std::max(longest, bins[x].size());
   PlannedItem filler = items.front();

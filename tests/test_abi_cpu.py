@@ -110,6 +110,11 @@ def _coverage(b, plan, P=None):
     return seen, want
 
 
+def _cost_class(cost) -> int:
+    """Octave of a planned item's cost in 64-unit steps."""
+    return int(max(1, int(cost) // 64)).bit_length() - 1
+
+
 @pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
 def test_plan_covers_each_row_head_once(lib, index):
     b = config_batch(index)
@@ -118,14 +123,15 @@ def test_plan_covers_each_row_head_once(lib, index):
     assert np.array_equal(seen, want)
     mat = plan[plan[:, 0] == 1]
     if len(mat) >= 16:
-        # matrix-core items: interleaved over 8 XCD bins (slot % 8); each bin runs longest first and
-        # keeps all items of one (request, KV head, partition) together
+        # matrix-core items: interleaved over 8 XCD bins (slot % 8); each bin runs its items by cost
+        # class (octave of the cost), longest first, and keeps all items of one (request, KV head,
+        # partition) on one XCD
         assert len(mat) % 8 == 0
         owner = {}
         for x in range(8):
             live = [row for row in mat[x::8] if row[4] > 0]
-            costs = [row[7] for row in live]
-            assert costs == sorted(costs, reverse=True)
+            classes = [_cost_class(row[7]) for row in live]
+            assert classes == sorted(classes, reverse=True)
             for row in live:
                 assert owner.setdefault((row[1], row[2], row[5]), x) == x
         assert np.all(mat[mat[:, 4] == 0][:, 7] == 0)    # fillers carry no work
@@ -334,7 +340,7 @@ def test_host_positions_balance_the_xcd_bins(lib):
 
 def test_host_positions_never_change_the_work_covered(lib):
     """Host positions only order the work: true, zero or arbitrary values plan every (row, head,
-    partition) exactly once, and each XCD bin still runs its longest items first."""
+    partition) exactly once, and each XCD bin still runs its longest cost classes first."""
     b = config_batch(3, num_reqs=12, max_hist=3000)
     rng = np.random.default_rng(3)
     junk = rng.integers(-2**31, 2**31 - 1, size=b.total_q, dtype=np.int64).astype(np.int32)
@@ -344,8 +350,8 @@ def test_host_positions_never_change_the_work_covered(lib):
         assert np.array_equal(seen, want)
         mat = plan[plan[:, 0] == 1]
         for x in range(8):
-            costs = [row[7] for row in mat[x::8] if row[4] > 0]
-            assert costs == sorted(costs, reverse=True)
+            classes = [_cost_class(row[7]) for row in mat[x::8] if row[4] > 0]
+            assert classes == sorted(classes, reverse=True)
     with pytest.raises(ValueError):
         desc_for(b, q_pos_host=b.q_pos[:-1])
 
