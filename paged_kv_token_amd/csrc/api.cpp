@@ -180,15 +180,14 @@ bool matrix_ok(const pensieve_batch_desc* d) {
 
 // Workgroup i of a launch runs on XCD i % kXcds, and each XCD has its own L2.
 // Matrix-core items of one (request, KV head, partition) stream the same K/V,
-// so they are kept on one XCD: such groups, longest first, go one by one to the
-// least loaded of kXcds bins; each bin then lists its items longest first, and
-// the bins are interleaved so that bin x occupies launch slots x, x + kXcds, ...
-// Bins are padded to equal length with zero-row items, which the kernel leaves
-// at once.
+// so they are kept on one XCD: such groups, costliest first, go one by one to
+// the least loaded of kXcds bins; each bin then lists its items by cost class,
+// longest first, and the bins are interleaved so that bin x occupies launch
+// slots x, x + kXcds, ...  Bins are padded to equal length with zero-row
+// items, which the kernel leaves at once.
 constexpr int kXcds = 8;
 
-// One (request, KV head, partition) of matrix-core items: items[first, first + count), all of
-// the same cost.
+// One (request, KV head, partition) of matrix-core items: items[first, first + count).
 struct ItemGroup {
   long long cost;   // total over the group's items
   int first, count;
