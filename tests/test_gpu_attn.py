@@ -187,3 +187,33 @@ def test_invalid_arguments_are_rejected_before_launch():
                              gb.cu_q_lens, None, torch.empty_like(gb.q),
                              torch.empty(1, dtype=torch.uint8, device="cuda"))
     assert ei.value.status == 3
+
+
+def test_host_positions_change_no_result():
+    """The optional host copy of the query positions only orders the work: the outputs with the
+    true copy, with none and with arbitrary values are bitwise equal, and match the oracle."""
+    import torch
+    from gpu_harness import poison_, to_host_storage
+    b = config_batch(3, num_reqs=6, max_hist=2500)
+    _say(f"host positions: {b.name} R={b.num_reqs} T={b.total_q}")
+    gb = upload(b)
+    junk = np.random.default_rng(5).integers(-2**31, 2**31 - 1, size=b.total_q, dtype=np.int64).astype(np.int32)
+    outs = []
+    for qp in (b.q_pos, None, junk, np.zeros(b.total_q, np.int32)):
+        desc = pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                            num_blocks=b.num_blocks, block_table_stride=b.block_table_stride, dtype=2,
+                            softmax_scale=b.softmax_scale, context_lens_host=b.context_lens,
+                            cu_q_lens_host=b.cu_q_lens, q_pos_host=qp)
+        ws = torch.empty(max(pk.pensieve_attn_workspace_size(desc), 256), dtype=torch.uint8, device="cuda")
+        ws.fill_(0xFF)
+        o = torch.empty_like(gb.q)
+        poison_(o, b.dtype)
+        pk.pensieve_attn_fwd(desc, gb.q, gb.k_pool, gb.v_pool, gb.block_tables, gb.context_lens, gb.cu_q_lens,
+                             gb.q_pos, o, ws)
+        torch.cuda.synchronize()
+        outs.append(o)
+    bits = [to_host_storage(o, b.dtype) for o in outs]
+    for other in bits[1:]:
+        assert np.array_equal(bits[0], other)
+    err = _max_err(to_f64(outs[0]), oracle_output(b))
+    assert err <= TOL[b.dtype], err
