@@ -384,7 +384,7 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(b, budget_s: float):
+def cpu_baseline(b, budget_s: float, min_s: float = MIN_CPU_S):
     """The CPU oracle (as it stands) on this host: all requests, as many query heads as fit the budget."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
@@ -401,7 +401,7 @@ def cpu_baseline(b, budget_s: float):
     # work (or the budget, if smaller) has been timed.
     done, elapsed = 0, 0.0
     chunk = 2
-    min_s = min(MIN_CPU_S, budget_s)
+    min_s = min(min_s, budget_s)
     while elapsed < budget_s and (done < b.num_heads or elapsed < min_s):
         first = done % b.num_heads
         heads = list(range(first, min(first + chunk, b.num_heads)))
@@ -417,6 +417,23 @@ def cpu_baseline(b, budget_s: float):
         what = f"all {b.num_reqs} requests x query heads 0..{done - 1} of {b.num_heads} (rate scaled to all heads)"
     return {"value": round(rate, 2), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{what} ({elapsed:.1f} s, float64 NumPy on {cpu_model()})"}
+
+
+def cpu_single_thread(budget_s: float = 3.0):
+    """The oracle with its BLAS limited to one thread on bounded samples of the tiny, 13B mixed and
+    decode-heavy workloads (their first requests, every query head), rates per query token."""
+    from threadpoolctl import threadpool_limits
+    out = []
+    for index, cut, what in ((0, {}, "all 3 requests"), (1, dict(num_reqs=8), "first 8 conversations + first 8 decode requests"),
+                             (2, dict(num_reqs=32), "first 32 of 256 requests")):
+        b = config_batch(index, **cut)
+        with threadpool_limits(limits=1):
+            r = cpu_baseline(b, budget_s, min_s=budget_s)
+        r["cores"] = 1
+        r["workload"] = b.name
+        r["sample"] = f"{what}: " + r["sample"]
+        out.append(r)
+    return out
 
 
 def secondary(index: int, steps: int, warmup: int, counters):
@@ -614,6 +631,8 @@ def main():
     if not args.no_cpu:
         log("cpu_baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+        log("oracle on one thread (tiny, 13B mixed and decode-heavy samples)")
+        result["cpu_single_thread"] = cpu_single_thread()
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
