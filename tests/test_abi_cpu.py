@@ -373,3 +373,20 @@ def test_vector_requests_beside_matrix_items_split_finer(lib):
             assert parts[r] == usual
         else:
             assert parts[r] >= 2 * usual - 1 and parts[r] > usual
+
+
+def test_xcd_bins_keep_a_requests_items_together_inside_a_cost_class(lib):
+    """Inside one XCD bin and one cost class, the items of one (request, KV head, partition) form a
+    single contiguous run, so they run close together and share that K/V in the XCD's L2."""
+    b = config_batch(3)
+    plan = pk.pensieve_debug_plan(desc_for(b, q_pos_host=b.q_pos))
+    mat = plan[plan[:, 0] == 1]
+    for x in range(8):
+        live = [row for row in mat[x::8] if row[4] > 0]
+        seen, prev = set(), None
+        for row in live:
+            key = (_cost_class(row[7]), int(row[1]), int(row[2]), int(row[5]))
+            if key != prev:
+                assert key not in seen, f"bin {x}: items of {key} split into two runs"
+                seen.add(key)
+            prev = key
