@@ -157,3 +157,55 @@ def test_append_runs_across_windows(dtype):
     torch.cuda.synchronize()
     assert np.array_equal(_bits(to_host_storage(k_pool, dtype)), _bits(k_ref))
     assert np.array_equal(_bits(to_host_storage(v_pool, dtype)), _bits(v_ref))
+
+
+def _random_run_slots(rng, nb: int) -> np.ndarray:
+    """Requests' new tokens as in-order runs from random block offsets; then pieces of that list
+    moved elsewhere (a block's tokens then arrive in several places), and some tokens skipped."""
+    blocks = iter(rng.permutation(nb).tolist())
+    slots = []
+    while len(slots) < int(rng.integers(40, 400)):
+        s = next(blocks) * 16 + int(rng.integers(0, 16))
+        for k in range(int(rng.integers(1, 70))):
+            if k > 0 and s % 16 == 0:
+                s = next(blocks) * 16
+            slots.append(s)
+            s += 1
+    slots = np.asarray(slots, dtype=np.int32)
+    for _ in range(int(rng.integers(0, 4))):
+        lo = int(rng.integers(0, len(slots)))
+        hi = min(len(slots), lo + int(rng.integers(1, 24)))
+        piece, rest = slots[lo:hi], np.concatenate([slots[:lo], slots[hi:]])
+        at = int(rng.integers(0, len(rest) + 1))
+        slots = np.concatenate([rest[:at], piece, rest[at:]]).astype(np.int32)
+    slots[rng.random(len(slots)) < 0.05] = -1
+    return slots
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_append_random_run_layouts(seed):
+    """Random run layouts (in order, pieces moved, skips), f16 d = 128 and f32 d = 64 alternately:
+    whole pools equal the oracle's append bit for bit."""
+    import torch
+    import paged_kv_token_amd as pk
+    from gpu_harness import poison_, to_device, torch_dtype
+    rng = np.random.default_rng(700 + seed)
+    dtype, d = ("f16", 128) if seed % 2 == 0 else ("f32", 64)
+    nb, hkv = 160, 2
+    slots = _random_run_slots(rng, nb)
+    n = len(slots)
+    sd = storage_dtype(dtype)
+    x = rng.standard_normal((2, n, hkv, d)).astype(np.float32)
+    k_new, v_new = (x[0].astype(np.float16), x[1].astype(np.float16)) if dtype == "f16" else (x[0], x[1])
+    fill = poison_fill(dtype)
+    k_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
+    v_ref = np.full((nb, hkv, d, 16), fill, dtype=sd)
+    oracle.append_kv(k_ref, v_ref, k_new, v_new, slots, 16)
+    _say(f"random runs seed {seed} {dtype}: n={n}")
+    k_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    v_pool = poison_(torch.empty((nb, hkv, d, 16), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    pk.pensieve_kv_append(to_device(k_new, dtype), to_device(v_new, dtype), k_pool, v_pool,
+                          torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(to_host_storage(k_pool, dtype)), _bits(k_ref))
+    assert np.array_equal(_bits(to_host_storage(v_pool, dtype)), _bits(v_ref))
