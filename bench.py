@@ -450,13 +450,15 @@ def secondary(index: int, steps: int, warmup: int, counters):
     out["query_tokens_per_s"] = round(b.total_q / (ms * 1e-3), 1)
     out["kernels_ms"] = {k: round(v["avg_ms"], 4) for k, v in per.items()}
     out["roofline"] = roofline_for(b, dev, per, dom, counters)
+    # The whole call against HBM: every request's K/V, Q, O and metadata once, over the call's time.
+    total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
+    out["attn_hbm_frac"] = round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     if index == 4:
         bufs = dev.split_buffers(32)
         ms2, trace2 = time_steps(lambda: dev.split_step(32, bufs), steps, warmup)
         per2 = summarize_trace(trace2, steps)
         out["split32_ms"] = round(ms2, 4)
         out["split32_kernels_ms"] = {k: round(v["avg_ms"], 4) for k, v in per2.items()}
-        total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
         out["split32_hbm_frac"] = round(total_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         del bufs
     del dev
