@@ -49,6 +49,20 @@
  *   sees keys 0..p.  Slots at positions >= context_lens[r], unused blocks and
  *   block-table entries past ceil(context_lens[r]/16) may hold any bits, NaN
  *   included; the output does not depend on them and they are never read.
+ * - Library-owned resources.  The library allocates no device memory on
+ *   the calls' paths (callers pass workspace), but keeps two kinds of
+ *   process-wide state, created on first use per device and held until the
+ *   process ends: (1) a ring of 32 page-locked, device-mapped host slots
+ *   (one 16 MiB slab, a slot grown alone past 512 KiB) through which
+ *   pensieve_attn_fwd, pensieve_attn_split_partial and the swaps upload
+ *   their host-built work lists with a small copy kernel on `stream`;
+ *   (2) a non-blocking side stream with two events: when a plan mixes
+ *   matrix-core and vector items and the matrix-core items alone cannot
+ *   fill the GPU, the vector items run on it, forked from and joined back
+ *   into `stream` with events (PENSIEVE_FLAG_SINGLE_STREAM keeps every
+ *   launch on `stream`).  Because work lists are built and uploaded at every call, the
+ *   calls refuse a stream that is being captured into a graph
+ *   (UNSUPPORTED).
  * - Errors: every call returns a status.  Problems visible on the host
  *   (null pointers, bad sizes, inconsistent host lengths, too small a
  *   workspace) return INVALID_ARG / UNSUPPORTED / WORKSPACE_TOO_SMALL before
@@ -97,6 +111,10 @@ typedef enum pensieve_dtype {
 /* pensieve_batch_desc.flags: pensieve_attn_fwd keeps every request whole (no
  * adaptive split-KV; no partials, no merge). */
 #define PENSIEVE_FLAG_NO_SPLIT 2
+/* pensieve_batch_desc.flags: every launch of the call stays on the caller's
+ * stream (no fork of vector items onto the library's side stream).  Results
+ * are identical either way. */
+#define PENSIEVE_FLAG_SINGLE_STREAM 4
 
 /* Shape of one unified batch plus host copies of its lengths (used to
  * validate and to plan the work; the device copies passed to the compute

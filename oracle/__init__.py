@@ -25,5 +25,4 @@ from .definitions import (  # noqa: F401
     split_merge,
     split_partial,
     to_f64,
-    visible_pairs,
 )

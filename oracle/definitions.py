@@ -308,21 +308,8 @@ def split_merge(part_o: np.ndarray, part_m: np.ndarray, part_l: np.ndarray) -> n
     return num / den
 
 
-# ---------------------------------------------------------------------------
-# Algorithmic work (used for reporting; not part of any check)
-# ---------------------------------------------------------------------------
-def visible_pairs(context_lens, cu_q_lens, q_pos) -> int:
-    """Number of (query row, key) pairs that the causal mask leaves visible."""
-    total = 0
-    for r in range(len(context_lens)):
-        lo, hi = int(cu_q_lens[r]), int(cu_q_lens[r + 1])
-        L = int(context_lens[r])
-        total += int((row_positions(q_pos, lo, hi, L) + 1).sum())
-    return total
-
-
 __all__ = [
     "to_f64", "e4m3_value", "e4m3_decode", "e4m3_encode", "quantize_e4m3", "E4M3_VALUES", "E4M3_MAX", "append_kv", "gather_kv", "kv_head_of", "causal_visible", "causal_attention",
     "default_positions", "row_positions", "paged_attention",
-    "partition_token_ranges", "partial_attention", "split_partial", "split_merge", "visible_pairs",
+    "partition_token_ranges", "partial_attention", "split_partial", "split_merge",
 ]

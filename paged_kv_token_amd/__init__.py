@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     PENSIEVE_F32,
     PENSIEVE_FP8_E4M3,
     PENSIEVE_FLAG_NO_SPLIT,
+    PENSIEVE_FLAG_SINGLE_STREAM,
     PENSIEVE_FLAG_VECTOR_ONLY,
     dtype_code,
     load_library,

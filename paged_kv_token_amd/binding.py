@@ -26,6 +26,7 @@ PENSIEVE_ERR_HIP = 4
 PENSIEVE_F32, PENSIEVE_F16, PENSIEVE_BF16, PENSIEVE_FP8_E4M3 = 0, 1, 2, 3
 PENSIEVE_FLAG_VECTOR_ONLY = 1
 PENSIEVE_FLAG_NO_SPLIT = 2
+PENSIEVE_FLAG_SINGLE_STREAM = 4
 
 EXPORTED = (
     "pensieve_version", "pensieve_last_error", "pensieve_kv_append", "pensieve_attn_workspace_size",
@@ -183,6 +184,50 @@ def make_desc(*, num_heads: int, num_kv_heads: int, head_dim: int, num_blocks: i
     return d
 
 
+def _shape(t, name: str, shape):
+    """Raise ValueError unless tensor t has exactly this shape (None entries match anything)."""
+    if t is None:
+        return
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        raise ValueError(f"{name} has shape {got}, expected {tuple('*' if w is None else w for w in shape)}")
+
+
+def _pool_shapes(k_pool, v_pool, num_blocks=None, hkv=None, d=None):
+    """K pool [NB][Hkv][16][d], V pool [NB][Hkv][d][16]; returns (NB, Hkv, d)."""
+    if k_pool.dim() != 4 or k_pool.shape[2] != 16:
+        raise ValueError(f"k_pool has shape {tuple(k_pool.shape)}, expected [num_blocks][Hkv][16][head_dim]")
+    nb, hk, _, dd = k_pool.shape
+    _shape(k_pool, "k_pool", (num_blocks, hkv, 16, d))
+    _shape(v_pool, "v_pool", (nb, hk, dd, 16))
+    return int(nb), int(hk), int(dd)
+
+
+def _check_batch(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos, o=None):
+    """Tensor shapes against the descriptor, before any pointer reaches the library."""
+    ctx, cu, _ = desc._keep
+    R = int(desc.num_reqs)
+    T = int(cu[-1]) if R > 0 else 0
+    _shape(q, "q", (T, desc.num_heads, desc.head_dim))
+    _shape(o, "o", (T, desc.num_heads, desc.head_dim))
+    if o is not None and q is not None and o.dtype != q.dtype:
+        raise ValueError(f"o holds {o.dtype}, q holds {q.dtype}")
+    _pool_shapes(k_pool, v_pool, desc.num_blocks, desc.num_kv_heads, desc.head_dim)
+    _shape(block_tables, "block_tables", (R, desc.block_table_stride))
+    _shape(context_lens, "context_lens", (R,))
+    _shape(cu_q_lens, "cu_q_lens", (R + 1,))
+    _shape(q_pos, "q_pos", (T,))
+
+
+def _check_append(k_new, v_new, k_pool, v_pool, slot_mapping):
+    if k_new.dim() != 3:
+        raise ValueError(f"k_new has shape {tuple(k_new.shape)}, expected [num_tokens][Hkv][head_dim]")
+    n, hkv, d = k_new.shape
+    _shape(v_new, "v_new", (n, hkv, d))
+    _pool_shapes(k_pool, v_pool, None, hkv, d)
+    _shape(slot_mapping, "slot_mapping", (n,))
+
+
 # ---- entry points --------------------------------------------------------------------
 def pensieve_version() -> str:
     return load_library().pensieve_version().decode()
@@ -191,6 +236,7 @@ def pensieve_version() -> str:
 def pensieve_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, stream=None):
     torch = _torch()
     lib = load_library()
+    _check_append(k_new, v_new, k_pool, v_pool, slot_mapping)
     n, hkv, d = k_new.shape
     nb = k_pool.shape[0]
     _check(lib.pensieve_kv_append(_ptr(k_new, "k_new"), _ptr(v_new, "v_new", k_new.dtype),
@@ -204,6 +250,7 @@ def pensieve_kv_append_fp8(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale: 
     """Append f16 / bf16 rows into E4M3 pools (uint8 or float8_e4m3fn tensors): code = E4M3(x / scale)."""
     torch = _torch()
     lib = load_library()
+    _check_append(k_new, v_new, k_pool, v_pool, slot_mapping)
     n, hkv, d = k_new.shape
     nb = k_pool.shape[0]
     _check(lib.pensieve_kv_append_fp8(_ptr(k_new, "k_new"), _ptr(v_new, "v_new", k_new.dtype),
@@ -233,7 +280,9 @@ def _kv_swap(fn, k_pool, v_pool, k_host, v_host, first, second, stream):
     s_arr, s_p = _block_list(second)
     if len(k_arr) != len(s_arr):
         raise ValueError("block lists differ in length")
-    _, hkv, _, d = k_pool.shape
+    _, hkv, d = _pool_shapes(k_pool, v_pool)
+    _shape(k_host, "k_host", (None,) + tuple(k_pool.shape[1:]))
+    _shape(v_host, "v_host", (k_host.shape[0],) + tuple(v_pool.shape[1:]))
     _check(fn(_ptr(k_pool, "k_pool"), _ptr(v_pool, "v_pool", k_pool.dtype), k_pool.shape[0],
               _host_ptr(k_host, "k_host", k_pool.dtype), _host_ptr(v_host, "v_host", k_pool.dtype), k_host.shape[0],
               k_p, s_p, len(k_arr), hkv, d, dtype_code(k_pool), _stream(stream)))
@@ -258,6 +307,7 @@ def pensieve_attn_workspace_size(desc: BatchDesc, num_partitions: int = 0) -> in
 def pensieve_attn_fwd(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos, o,
                       workspace, stream=None):
     torch = _torch()
+    _check_batch(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos, o)
     _check(load_library().pensieve_attn_fwd(
         ctypes.byref(desc), _ptr(q, "q"), _pool_ptr(k_pool, "k_pool", desc), _pool_ptr(v_pool, "v_pool", desc),
         _ptr(block_tables, "block_tables", torch.int32), _ptr(context_lens, "context_lens", torch.int32),
@@ -269,6 +319,11 @@ def pensieve_attn_fwd(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_
 def pensieve_attn_split_partial(desc: BatchDesc, num_partitions: int, q, k_pool, v_pool, block_tables,
                                 context_lens, cu_q_lens, q_pos, part_o, part_m, part_l, workspace, stream=None):
     torch = _torch()
+    _check_batch(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos)
+    T, P = int(q.shape[0]), int(num_partitions)
+    _shape(part_o, "part_o", (T, desc.num_heads, P, desc.head_dim))
+    _shape(part_m, "part_m", (T, desc.num_heads, P))
+    _shape(part_l, "part_l", (T, desc.num_heads, P))
     _check(load_library().pensieve_attn_split_partial(
         ctypes.byref(desc), num_partitions, _ptr(q, "q"), _pool_ptr(k_pool, "k_pool", desc),
         _pool_ptr(v_pool, "v_pool", desc), _ptr(block_tables, "block_tables", torch.int32),
@@ -282,6 +337,9 @@ def pensieve_attn_split_partial(desc: BatchDesc, num_partitions: int, q, k_pool,
 def pensieve_attn_split_merge(part_o, part_m, part_l, o, stream=None):
     torch = _torch()
     t, hq, p, d = part_o.shape
+    _shape(part_m, "part_m", (t, hq, p))
+    _shape(part_l, "part_l", (t, hq, p))
+    _shape(o, "o", (t, hq, d))
     _check(load_library().pensieve_attn_split_merge(
         _ptr(part_o, "part_o", torch.float32), _ptr(part_m, "part_m", torch.float32),
         _ptr(part_l, "part_l", torch.float32), t, hq, d, p, dtype_code(o), _ptr(o, "o"), _stream(stream)))

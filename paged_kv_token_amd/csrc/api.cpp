@@ -111,7 +111,7 @@ pensieve_status check_desc(const pensieve_batch_desc* d) {
   if (d->num_blocks <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "num_blocks must be > 0");
   if (d->block_table_stride <= 0) return fail(PENSIEVE_ERR_INVALID_ARG, "block_table_stride must be > 0");
   if (!(d->softmax_scale > 0.f)) return fail(PENSIEVE_ERR_INVALID_ARG, "softmax_scale must be > 0");
-  if (d->flags & ~(PENSIEVE_FLAG_VECTOR_ONLY | PENSIEVE_FLAG_NO_SPLIT))
+  if (d->flags & ~(PENSIEVE_FLAG_VECTOR_ONLY | PENSIEVE_FLAG_NO_SPLIT | PENSIEVE_FLAG_SINGLE_STREAM))
     return fail(PENSIEVE_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
   if (d->num_reqs > 0 && (!d->context_lens_host || !d->cu_q_lens_host))
     return fail(PENSIEVE_ERR_INVALID_ARG, "context_lens_host / cu_q_lens_host is NULL");
@@ -444,6 +444,7 @@ struct Stager {
     bool owned = false;       // a buffer of its own (else a slice of the slab)
     hipEvent_t ev = nullptr;
     bool pending = false;
+    bool in_use = false;      // handed out by stage_acquire, not yet given back by stage_release
   };
   std::mutex mu;
   Slot slots[kSlots];
@@ -490,8 +491,15 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
       st->slots[i].cap = Stager::kSlotBytes;
     }
   }
-  Stager::Slot& s = st->slots[st->next];
-  st->next = (st->next + 1) % Stager::kSlots;
+  // The next slot that no other call holds between its acquire and its release.
+  int pick = -1;
+  for (int k = 0; k < Stager::kSlots && pick < 0; ++k) {
+    const int i = (st->next + k) % Stager::kSlots;
+    if (!st->slots[i].in_use) pick = i;
+  }
+  if (pick < 0) return hipErrorNotReady;   // every slot is held by a call still enqueueing its work
+  Stager::Slot& s = st->slots[pick];
+  st->next = (pick + 1) % Stager::kSlots;
   if (s.pending) {
     if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return e;
     s.pending = false;
@@ -511,6 +519,7 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   }
   if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
   std::memcpy(s.host, src, bytes);
+  s.in_use = true;
   *mapped = s.mapped;
   *slot_out = &s;
   return hipSuccess;
@@ -522,6 +531,7 @@ hipError_t stage_release(Stager::Slot* slot, hipStream_t stream) {
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
   std::lock_guard<std::mutex> lk(st->mu);
+  slot->in_use = false;
   if ((e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
   slot->pending = true;
   return hipSuccess;
@@ -537,8 +547,26 @@ hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t
     e = pk::launch_stage_copy(mapped, dst, bytes, stream);
   else
     e = hipMemcpyAsync(dst, slot->host, bytes, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return e;
-  return stage_release(slot, stream);
+  const hipError_t e2 = stage_release(slot, stream);   // gives the slot back even after a failed launch
+  return e != hipSuccess ? e : e2;
+}
+
+// How a plan's work list reaches the device.
+enum class Upload {
+  kStaged,     // the pinned staging ring (allocated by the library on first use) and a copy kernel
+  kPageable,   // a plain host-to-device copy from pageable host memory; allocates nothing
+};
+
+// Host-visible misuse: the staged work lists and the library's side stream do not survive
+// graph capture (a captured graph would replay a stale list), so capture is refused.
+pensieve_status refuse_capture(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, "stream capture query");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(PENSIEVE_ERR_UNSUPPORTED, "the stream is being captured into a graph; the calls plan and upload "
+                                          "their work list at every call and cannot be captured");
+  return PENSIEVE_OK;
 }
 
 // ---- per-launch timing trace ------------------------------------------------------------
@@ -660,11 +688,16 @@ int device_cu_count() {
 }
 
 pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::AttnArgs& args, void* workspace,
-                         hipStream_t stream) {
+                         hipStream_t stream, Upload upload = Upload::kStaged) {
   uint8_t* const ws = static_cast<uint8_t*>(workspace);
+  auto to_device = [&](const void* src, size_t bytes) -> hipError_t {
+    if (upload == Upload::kStaged) return stage_to_device(ws, src, bytes, stream);
+    // Pageable source: the copy has taken the bytes when the call returns.
+    return bytes ? hipMemcpyAsync(ws, src, bytes, hipMemcpyHostToDevice, stream) : hipSuccess;
+  };
   hipError_t e;
   if (plan.split_rows == 0) {
-    e = stage_to_device(ws, plan.items.data(), plan.items.size() * sizeof(pk::WorkItem), stream);
+    e = to_device(plan.items.data(), plan.items.size() * sizeof(pk::WorkItem));
   } else {
     // Items, partial base rows and the partial row map go up in one copy; the partials of
     // the split requests live in the rest of the workspace and are merged at the end.
@@ -672,7 +705,7 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     std::memcpy(meta.data(), plan.items.data(), plan.items.size() * sizeof(pk::WorkItem));
     std::memcpy(meta.data() + plan.base_off(), plan.part_row_base.data(), plan.part_row_base.size() * sizeof(int32_t));
     std::memcpy(meta.data() + plan.rowmap_off(), plan.rowmap.data(), plan.rowmap.size() * sizeof(int32_t));
-    e = stage_to_device(ws, meta.data(), meta.size(), stream);
+    e = to_device(meta.data(), meta.size());
     args.part_row_base = reinterpret_cast<const int32_t*>(ws + plan.base_off());
     args.part_m = reinterpret_cast<float*>(ws + plan.pm_off());
     args.part_l = reinterpret_cast<float*>(ws + plan.pl_off());
@@ -689,7 +722,10 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
   int matrix_items = 0;
   for (const Segment& s : plan.segments)
     if (s.kernel == kMatrix) matrix_items += s.count;
-  const bool fork = has_matrix && has_vector && matrix_items < 2 * device_cu_count();
+  // Single-stream mode (the flag, or a call that must allocate nothing, since the side stream is
+  // created on first use) keeps every launch on the caller's stream.
+  const bool single = (d->flags & PENSIEVE_FLAG_SINGLE_STREAM) || upload == Upload::kPageable;
+  const bool fork = !single && has_matrix && has_vector && matrix_items < 2 * device_cu_count();
   std::unique_lock<std::mutex> side_lock;
   if (fork) {
     if ((e = concurrency_for_current_device(&conc)) != hipSuccess) return hip_fail(e, "side stream");
@@ -796,6 +832,7 @@ pensieve_status kv_swap(bool to_host, void* k_pool, void* v_pool, int32_t num_bl
     return fail(PENSIEVE_ERR_INVALID_ARG, "k_host / v_host must be page-locked host memory mapped for the device");
   const int64_t block_bytes = (int64_t)num_kv_heads * kBlockSize * head_dim * elem_bytes(dtype);
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pensieve_status s = refuse_capture(st); s != PENSIEVE_OK) return s;
   void* pairs_map = nullptr;
   Stager::Slot* slot = nullptr;
   hipError_t e = stage_acquire(pairs.data(), pairs.size() * sizeof(int32_t), &pairs_map, &slot);
@@ -807,8 +844,9 @@ pensieve_status kv_swap(bool to_host, void* k_pool, void* v_pool, int32_t num_bl
                 : pk::launch_kv_swap(k_map, v_map, k_pool, v_pool, static_cast<const int32_t*>(pairs_map), n,
                                      block_bytes, st);
   }
+  const hipError_t e2 = stage_release(slot, st);   // gives the slot back even after a failed launch
   if (e != hipSuccess) return hip_fail(e, "kv swap launch");
-  if ((e = stage_release(slot, st)) != hipSuccess) return hip_fail(e, "block list staging");
+  if (e2 != hipSuccess) return hip_fail(e2, "block list staging");
   return ok();
 }
 
@@ -912,6 +950,7 @@ pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q
   if (total_q(desc) == 0) return ok();
   if (!o) return fail(PENSIEVE_ERR_INVALID_ARG, "o is NULL");
   if (o == q) return fail(PENSIEVE_ERR_INVALID_ARG, "o must not alias q");
+  if ((s = refuse_capture(static_cast<hipStream_t>(stream))) != PENSIEVE_OK) return s;
   thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, 0, plan);
   if (!workspace || workspace_bytes < plan.bytes())
@@ -936,6 +975,7 @@ pensieve_status pensieve_attn_split_partial(const pensieve_batch_desc* desc, int
   if ((s = check_attn_pointers(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens)) != PENSIEVE_OK) return s;
   if (total_q(desc) == 0) return ok();
   if (!part_o || !part_m || !part_l) return fail(PENSIEVE_ERR_INVALID_ARG, "a partial buffer is NULL");
+  if ((s = refuse_capture(static_cast<hipStream_t>(stream))) != PENSIEVE_OK) return s;
   thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, num_partitions, plan);
   if (!workspace || workspace_bytes < plan.bytes())

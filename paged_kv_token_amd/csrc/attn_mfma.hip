@@ -138,14 +138,14 @@ constexpr int lgkmcnt0_imm() { return 63 | (3 << 14) | (7 << 4); }
 // it read as zero) straight into LDS at `lds_dst + 16 * lane`.  Issued as inline assembly
 // so that the compiler's wait-count tracking, which cannot tell one LDS stage from another,
 // does not wait for these loads before every LDS read; callers wait for them explicitly
-// with s_waitcnt vmcnt.  M0 carries the LDS address; nothing else in these kernels uses M0.
+// with s_waitcnt vmcnt.  M0 carries the LDS address, bound as an input operand, so the
+// compiler itself writes it and knows it holds that value.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t nbytes, uint32_t voff, uint8_t* lds_dst) {
   const unsigned long long b = (unsigned long long)base;
   const i32x4 rsrc = {(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)nbytes, kBufferWord3};
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(m0)
-               : "memory");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
 }
 
 // Workgroup barrier that does not wait for outstanding memory operations (LDS-DMA

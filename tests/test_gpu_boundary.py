@@ -1,0 +1,99 @@
+"""The C-ABI boundary on the GPU: shape checks in the binding, refusal of graph capture, and the
+single-stream flag (every launch on the caller's stream gives the same bits as the forked plan)."""
+
+import numpy as np
+import pytest
+
+import paged_kv_token_amd as pk
+from gpu_harness import run_attn, to_host_storage, upload
+from workloads import custom_batch
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[boundary] {msg}", flush=True)
+
+
+def _mixed():
+    # Prefill rows (matrix cores) beside decode rows (vector kernel): the default plan forks.
+    return custom_batch([300, 1200, 0, 500], [40, 1, 12, 1], num_heads=4, num_kv_heads=4, head_dim=128,
+                        dtype="f16", seed=61)
+
+
+def test_single_stream_flag_is_bitwise_equal():
+    b = _mixed()
+    gb = upload(b)
+    plan = pk.pensieve_debug_plan(gb.desc)
+    assert {int(k) for k in plan[:, 0]} == {0, 1}, "the batch should have both kinds of items"
+    a = to_host_storage(run_attn(gb), b.dtype)
+    s = to_host_storage(run_attn(gb, pk.PENSIEVE_FLAG_SINGLE_STREAM), b.dtype)
+    assert np.array_equal(a, s)
+
+
+def test_binding_rejects_mismatched_shapes():
+    import torch
+    b = _mixed()
+    gb = upload(b)
+    ws = torch.empty(max(pk.pensieve_attn_workspace_size(gb.desc), 256), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(gb.q)
+    args = dict(q=gb.q, k_pool=gb.k_pool, v_pool=gb.v_pool, block_tables=gb.block_tables,
+                context_lens=gb.context_lens, cu_q_lens=gb.cu_q_lens, q_pos=gb.q_pos, o=o, workspace=ws)
+    bad = {
+        "q": gb.q[:-1].contiguous(),
+        "o": torch.empty((b.total_q, b.num_heads, b.head_dim // 2), dtype=gb.q.dtype, device="cuda"),
+        "k_pool": gb.k_pool[:-1].contiguous(),
+        "v_pool": gb.v_pool.transpose(2, 3).contiguous(),
+        "block_tables": gb.block_tables[:, :-1].contiguous(),
+        "context_lens": gb.context_lens[:-1].contiguous(),
+        "cu_q_lens": gb.cu_q_lens[:-1].contiguous(),
+        "q_pos": torch.zeros(b.total_q + 1, dtype=torch.int32, device="cuda"),
+    }
+    for name, t in bad.items():
+        kw = dict(args)
+        kw[name] = t
+        with pytest.raises(ValueError):
+            pk.pensieve_attn_fwd(gb.desc, **kw)
+        _say(f"{name}: rejected")
+    with pytest.raises(ValueError):
+        pk.pensieve_kv_append(gb.k_new, gb.v_new[:-1].contiguous(), gb.k_pool, gb.v_pool, gb.new_slots)
+    with pytest.raises(ValueError):
+        pk.pensieve_kv_append(gb.k_new, gb.v_new, gb.k_pool, gb.v_pool, gb.new_slots[:-1].contiguous())
+    k_host = torch.empty((4,) + tuple(gb.k_pool.shape[1:]), dtype=gb.k_pool.dtype).pin_memory()
+    v_host = torch.empty((5,) + tuple(gb.v_pool.shape[1:]), dtype=gb.v_pool.dtype).pin_memory()
+    with pytest.raises(ValueError):
+        pk.pensieve_kv_swap_out(gb.k_pool, gb.v_pool, k_host, v_host, [0], [1])
+    torch.cuda.synchronize()
+
+
+def test_graph_capture_is_refused():
+    """The calls build and upload their work list per call, so a capturing stream is refused before
+    anything is enqueued (nothing of ours enters the graph)."""
+    import torch
+    b = _mixed()
+    gb = upload(b)
+    ws = torch.empty(max(pk.pensieve_attn_workspace_size(gb.desc), 256), dtype=torch.uint8, device="cuda")
+    o = torch.zeros_like(gb.q)
+    x = torch.zeros(16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    status = None
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        try:
+            x.add_(1.0)
+            try:
+                pk.pensieve_attn_fwd(gb.desc, gb.q, gb.k_pool, gb.v_pool, gb.block_tables, gb.context_lens,
+                                     gb.cu_q_lens, gb.q_pos, o, ws, stream=side)
+            except pk.PensieveError as e:
+                status = e.status
+        finally:
+            g.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert status == pk.PENSIEVE_ERR_UNSUPPORTED
+    g.replay()
+    torch.cuda.synchronize()
+    assert float(x[0]) == 1.0
+    assert not torch.any(o != 0)
