@@ -50,7 +50,7 @@
  *   block-table entries past ceil(context_lens[r]/16) may hold any bits, NaN
  *   included; the output does not depend on them and they are never read.
  * - Library-owned resources.  The library allocates no device memory on
- *   the calls' paths (callers pass workspace), but keeps two kinds of
+ *   the calls' paths (callers pass workspace), but keeps three kinds of
  *   process-wide state, created on first use per device and held until the
  *   process ends: (1) a ring of 32 page-locked, device-mapped host slots
  *   (one 16 MiB slab, a slot grown alone past 512 KiB) through which
@@ -60,7 +60,9 @@
  *   matrix-core and vector items and the matrix-core items alone cannot
  *   fill the GPU, the vector items run on it, forked from and joined back
  *   into `stream` with events (PENSIEVE_FLAG_SINGLE_STREAM keeps every
- *   launch on `stream`).  Because work lists are built and uploaded at every call, the
+ *   launch on `stream`); (3) the device scratch array of
+ *   pensieve_attn_fwd_noalloc (64 MiB per GPU, allocated with the code
+ *   object).  Because work lists are built and uploaded at every call, the
  *   calls refuse a stream that is being captured into a graph
  *   (UNSUPPORTED).
  * - Errors: every call returns a status.  Problems visible on the host
@@ -323,6 +325,28 @@ pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q
                                   const int32_t* context_lens, const int32_t* cu_q_lens,
                                   const int32_t* q_pos, void* o, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * pensieve_attn_fwd without a workspace, for callers that cannot allocate
+ * device memory (code that may not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and kernels
+ * as pensieve_attn_fwd, and bitwise the same output; the work list and the
+ * split partials live in a library-owned device array of 64 MiB per GPU
+ * instead of a caller workspace.  The call allocates nothing (no hipMalloc,
+ * hipHostMalloc, stream or event creation): it runs every launch on
+ * `stream` (as with PENSIEVE_FLAG_SINGLE_STREAM) and copies the work list
+ * from pageable host memory with hipMemcpyAsync, which may wait for earlier
+ * work on `stream` before it returns.  A batch whose work list and partials
+ * exceed 64 MiB returns WORKSPACE_TOO_SMALL (pensieve_attn_workspace_size
+ * reports the bytes it would need).  Every call on one GPU shares that GPU's
+ * array: calls on one stream are ordered, but calls that may overlap on one
+ * GPU (several streams or host threads) race and must not be issued.  A
+ * stream being captured into a graph is refused (UNSUPPORTED).
+ */
+pensieve_status pensieve_attn_fwd_noalloc(const pensieve_batch_desc* desc, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables,
+                                          const int32_t* context_lens, const int32_t* cu_q_lens,
+                                          const int32_t* q_pos, void* o, void* stream);
 
 /*
  * Split-KV partials (PersistentKV, section 2: one long context cut into

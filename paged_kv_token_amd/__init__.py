@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     conversations,
     make_desc,
     pensieve_attn_fwd,
+    pensieve_attn_fwd_noalloc,
     pensieve_attn_split_merge,
     pensieve_attn_split_partial,
     pensieve_attn_workspace_size,

@@ -33,6 +33,7 @@ EXPORTED = (
     "pensieve_attn_fwd", "pensieve_attn_split_partial", "pensieve_attn_split_merge", "pensieve_debug_plan",
     "pensieve_trace_enable", "pensieve_trace_read", "pensieve_kv_swap_out", "pensieve_kv_swap_in",
     "pensieve_cache_plan_evictions", "pensieve_cache_build_batch", "pensieve_kv_append_fp8",
+    "pensieve_attn_fwd_noalloc",
 )
 TRACE_KERNELS = {0: "kv_append", 1: "attn_vector", 2: "attn_mfma", 3: "split_merge", 4: "kv_swap"}
 
@@ -97,6 +98,7 @@ def load_library(path: Optional[str] = None):
     lib.pensieve_kv_swap_in.argtypes = [vp, vp, i32, vp, vp, i32, i32p, i32p, i32, i32, i32, i32, vp]
     lib.pensieve_attn_workspace_size.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.pensieve_attn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.pensieve_attn_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.pensieve_attn_split_partial.argtypes = [dp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 ctypes.c_size_t, vp]
     lib.pensieve_attn_split_merge.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
@@ -313,6 +315,18 @@ def pensieve_attn_fwd(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_
         _ptr(block_tables, "block_tables", torch.int32), _ptr(context_lens, "context_lens", torch.int32),
         _ptr(cu_q_lens, "cu_q_lens", torch.int32), _ptr(q_pos, "q_pos", torch.int32), _ptr(o, "o", q.dtype),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size() if workspace is not None else 0,
+        _stream(stream)))
+
+
+def pensieve_attn_fwd_noalloc(desc: BatchDesc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos, o,
+                              stream=None):
+    """pensieve_attn_fwd with the library's own device scratch instead of a workspace (allocates nothing)."""
+    torch = _torch()
+    _check_batch(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos, o)
+    _check(load_library().pensieve_attn_fwd_noalloc(
+        ctypes.byref(desc), _ptr(q, "q"), _pool_ptr(k_pool, "k_pool", desc), _pool_ptr(v_pool, "v_pool", desc),
+        _ptr(block_tables, "block_tables", torch.int32), _ptr(context_lens, "context_lens", torch.int32),
+        _ptr(cu_q_lens, "cu_q_lens", torch.int32), _ptr(q_pos, "q_pos", torch.int32), _ptr(o, "o", q.dtype),
         _stream(stream)))
 
 

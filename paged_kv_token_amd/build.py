@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpensieve.so")
 
 SOURCES = ["api.cpp", "kv_append.hip", "attn_vector.hip", "attn_mfma.hip", "split_merge.hip", "stage_copy.hip", "kv_swap.hip",
-           "cache_plan.cpp"]
+           "cache_plan.cpp", "scratch.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

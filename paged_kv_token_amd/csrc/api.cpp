@@ -963,6 +963,31 @@ pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q
   return run_plan(desc, plan, a, workspace, static_cast<hipStream_t>(stream));
 }
 
+pensieve_status pensieve_attn_fwd_noalloc(const pensieve_batch_desc* desc, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_tables, const int32_t* context_lens,
+                                          const int32_t* cu_q_lens, const int32_t* q_pos, void* o, void* stream) {
+  pensieve_status s = check_desc(desc);
+  if (s != PENSIEVE_OK) return s;
+  if ((s = check_attn_pointers(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens)) != PENSIEVE_OK) return s;
+  if (total_q(desc) == 0) return ok();
+  if (!o) return fail(PENSIEVE_ERR_INVALID_ARG, "o is NULL");
+  if (o == q) return fail(PENSIEVE_ERR_INVALID_ARG, "o must not alias q");
+  if ((s = refuse_capture(static_cast<hipStream_t>(stream))) != PENSIEVE_OK) return s;
+  thread_local Plan plan;   // keeps its capacity from call to call
+  build_plan(desc, 0, plan);
+  if (plan.bytes() > pk::kScratchBytes)
+    return fail(PENSIEVE_ERR_WORKSPACE_TOO_SMALL, "the batch needs %zu bytes of scratch; the library's scratch holds %zu",
+                plan.bytes(), pk::kScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = pk::scratch_for_current_device(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  pk::AttnArgs a = make_args(desc, q, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos);
+  a.o = static_cast<uint8_t*>(o);
+  a.write_partials = 0;
+  a.part_stride = 1;
+  return run_plan(desc, plan, a, scratch, static_cast<hipStream_t>(stream), Upload::kPageable);
+}
+
 pensieve_status pensieve_attn_split_partial(const pensieve_batch_desc* desc, int32_t num_partitions, const void* q,
                                             const void* k_pool, const void* v_pool, const int32_t* block_tables,
                                             const int32_t* context_lens, const int32_t* cu_q_lens,

@@ -58,6 +58,13 @@ hipError_t launch_stage_copy(const void* src_mapped, void* dst, size_t bytes, hi
 
 // Merge of split partials into O: rows = partial rows x num_heads; rowmap
 // (nullable) gives each partial row's output row and partition count.
+// Size of the library-owned device scratch of pensieve_attn_fwd_noalloc (one array per GPU).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+
+// Device address of this GPU's scratch array (looked up once per device, with that device
+// current, and kept).
+hipError_t scratch_for_current_device(void** ptr);
+
 hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows, int num_heads,
                               int head_dim, int num_partitions, const int32_t* rowmap, int dtype, void* o,
                               hipStream_t stream);
