@@ -1,0 +1,77 @@
+"""Structured parity at the long-context workload's real lengths (32k-65k keys).
+
+"PersistentKV: Page-Aware Decode Scheduling for Long-Context LLM Serving on Commodity GPUs",
+section 2 (one long context cut into partitions).  Zero-query signature values and one-hot rows
+(tests/long_cases.py) make a single wrong block or a slipped causal boundary show up far beyond
+the gate at every length (the margins are derived on the CPU in test_long_context_pins.py).
+Every case runs with both kernels (default routing, vector only) and three plans: never split
+(whole partitions of up to 1025 tiles, so the matrix-core kernel streams far past its first 128
+tiles), the adaptive split of pensieve_attn_fwd, and the explicit 32-way split pair.
+"""
+
+import numpy as np
+import pytest
+
+import paged_kv_token_amd as pk
+from gpu_harness import run_attn, run_split, to_f64, upload
+from long_cases import ONEHOT_TOL, onehot_batch, onehot_expected, signature_batch, signature_expected, signature_tol
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = {"default": 0, "vector": pk.PENSIEVE_FLAG_VECTOR_ONLY}
+PLANS = ("no_split", "adaptive", "split32")
+
+
+def _say(msg):
+    print(f"[long] {msg}", flush=True)
+
+
+def _run(gb, plan, kflag):
+    if plan == "split32":
+        return to_f64(run_split(gb, 32, kflag)[3])
+    return to_f64(run_attn(gb, kflag | (pk.PENSIEVE_FLAG_NO_SPLIT if plan == "no_split" else 0)))
+
+
+def _longest_matrix_partition_tiles(gb):
+    """Tiles (64 keys) of the longest partition any matrix-core item streams, unsplit plan."""
+    plan = pk.pensieve_debug_plan(gb.make_desc(pk.PENSIEVE_FLAG_NO_SPLIT))
+    b = gb.batch
+    best = 0
+    for kern, r, g, q0, qc, part, nparts, cost, h0, hc in plan:
+        if kern == 1 and qc > 0:
+            best = max(best, -(-int(b.context_lens[r]) // 64))
+    return best
+
+
+@pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8), ("f16", 1)])
+def test_signature_zero_query_at_long_lengths(dtype, group):
+    b = signature_batch(dtype, group)
+    _say(f"signature {dtype} G={group}: L={b.context_lens.tolist()} T={b.total_q}")
+    gb = upload(b)
+    assert _longest_matrix_partition_tiles(gb) > 128
+    exp = signature_expected(b)
+    tol = signature_tol(exp, dtype)
+    for kname, kflag in KERNELS.items():
+        for plan in PLANS:
+            got = _run(gb, plan, kflag)
+            assert np.all(np.isfinite(got)), (kname, plan)
+            bad = np.abs(got - exp) > tol
+            worst = float(np.max(np.abs(got - exp) / tol))
+            _say(f"  {kname}/{plan}: worst |err|/tol {worst:.3f}")
+            assert not bad.any(), (kname, plan, np.argwhere(bad)[:5].tolist())
+
+
+@pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8), ("f16", 1)])
+def test_onehot_rows_in_every_tile(dtype, group):
+    b = onehot_batch(dtype, group)
+    _say(f"one-hot {dtype} G={group}: L={b.context_lens.tolist()} rows per request {b.q_lens.tolist()}")
+    gb = upload(b)
+    assert gb.q_pos is not None
+    assert _longest_matrix_partition_tiles(gb) > 128
+    exp = onehot_expected(b)
+    for kname, kflag in KERNELS.items():
+        for plan in PLANS:
+            got = _run(gb, plan, kflag)
+            err = np.abs(got - exp)
+            _say(f"  {kname}/{plan}: max abs err {float(err.max()):.3e}")
+            assert np.all(np.isfinite(got)) and float(err.max()) <= ONEHOT_TOL, (kname, plan)

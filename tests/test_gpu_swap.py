@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import paged_kv_token_amd as pk
-from gpu_harness import run_attn, torch_dtype, upload
+from gpu_harness import run_attn, to_f64, to_host_storage, upload
+from oracle_helpers import oracle_output, oracle_pools
 from workloads import config_batch, custom_batch
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +75,18 @@ def test_round_trip_leaves_attention_bitwise_unchanged(name):
     torch.cuda.synchronize()
     after = run_attn(gb)
     assert np.array_equal(_bits(before), _bits(after)), "attention changed after the round trip"
+    # Against the oracle: the moved blocks hold exactly what the oracle's append put in the original
+    # ones (NaN poison in stale slots included), and attention over them meets the gate.
+    ok_pool, ov_pool = oracle_pools(b)
+    idx = torch.from_numpy(new_ids).cuda().long()
+    for got, want in ((gb.k_pool[idx], ok_pool[used]), (gb.v_pool[idx], ov_pool[used])):
+        got = to_host_storage(got, b.dtype)
+        assert got.shape == want.shape
+        assert np.array_equal(got, want, equal_nan=b.dtype != "bf16"), "moved blocks differ from the oracle's"
+    tol = 1e-4 if b.dtype == "f32" else 1e-2
+    err = float(np.max(np.abs(to_f64(after) - oracle_output(b))))
+    _say(f"{name}: blocks bit-exact vs oracle pools, attention max abs err {err:.2e}")
+    assert err <= tol
 
 
 def test_swap_in_on_a_second_stream_beside_attention():

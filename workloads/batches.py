@@ -104,6 +104,10 @@ class Batch:
     q_fn: Optional[Callable[[int], np.ndarray]] = field(default=None, repr=False)
     k_fn: Optional[Callable[[int], np.ndarray]] = field(default=None, repr=False)
     v_fn: Optional[Callable[[int], np.ndarray]] = field(default=None, repr=False)
+    # Optional explicit query positions per request (sorted, distinct, each below the request's
+    # context length); they replace the recompute/new-row convention above: the request's rows
+    # sit at these positions and every other position of [0, L_r) is cached history.
+    positions: Optional[list] = field(default=None, repr=False)
 
     # ---- shapes -----------------------------------------------------------
     @property
@@ -116,6 +120,8 @@ class Batch:
 
     @property
     def q_lens(self) -> np.ndarray:
+        if self.positions is not None:
+            return np.array([len(p) for p in self.positions], dtype=np.int32)
         return (self.evict_lens + self.new_lens).astype(np.int32)
 
     @property
@@ -141,10 +147,14 @@ class Batch:
         return DTYPE_BYTES[self.dtype]
 
     def query_positions(self, r: int) -> np.ndarray:
+        if self.positions is not None:
+            return np.asarray(self.positions[r], dtype=np.int64)
         e, h, n = int(self.evict_lens[r]), int(self.hist_lens[r]), int(self.new_lens[r])
         return np.concatenate([np.arange(0, e), np.arange(h, h + n)]).astype(np.int64)
 
     def cached_positions(self, r: int) -> np.ndarray:
+        if self.positions is not None:
+            return np.setdiff1d(np.arange(int(self.context_lens[r]), dtype=np.int64), self.query_positions(r))
         return np.arange(int(self.evict_lens[r]), int(self.hist_lens[r]), dtype=np.int64)
 
     @property
@@ -156,6 +166,11 @@ class Batch:
     @property
     def has_default_positions(self) -> bool:
         """True when every request's rows are its last q_r positions."""
+        if self.positions is not None:
+            return all(np.array_equal(self.query_positions(r),
+                                      np.arange(int(self.context_lens[r]) - int(self.q_lens[r]),
+                                                int(self.context_lens[r])))
+                       for r in range(self.num_reqs))
         return bool(np.all(self.evict_lens == 0))
 
     def slots_for(self, r: int, positions: np.ndarray) -> np.ndarray:
