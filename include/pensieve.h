@@ -72,7 +72,13 @@
  *   pensieve_last_error() then describes the failure (per thread).
  *   The contents of device arrays are the caller's contract: slots and block
  *   ids in range, no duplicate slot in one append, query positions strictly
- *   increasing within a request and below its context length.
+ *   increasing within a request and below its context length, device length
+ *   arrays equal to their host copies.  With PENSIEVE_DEBUG=1 in the
+ *   environment (read at every call), pensieve_kv_append(_fp8) and the
+ *   attention calls first copy those device arrays to the host (waiting for
+ *   `stream`) and return INVALID_ARG on a violation before anything of the
+ *   call is enqueued; they never read the pools to do so.  Debugging and
+ *   tests only: it synchronises every call.
  */
 #ifndef PENSIEVE_H
 #define PENSIEVE_H

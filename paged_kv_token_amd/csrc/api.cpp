@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <deque>
 #include <mutex>
@@ -850,6 +851,88 @@ pensieve_status kv_swap(bool to_host, void* k_pool, void* v_pool, int32_t num_bl
   return ok();
 }
 
+// ---- device-contract validator (PENSIEVE_DEBUG=1) -------------------------------------------
+// The contents of device arrays are the caller's contract: slots and block ids in range, no
+// duplicate slot in one append, host copies equal to the device arrays, query positions strictly
+// increasing within a request and below its context length.  With PENSIEVE_DEBUG=1 in the
+// environment every append and attention call first copies those arrays to the host (waiting for
+// the stream) and returns INVALID_ARG on a violation, before anything of the call is enqueued.
+// It reads metadata only, never the pools; it is for tests and debugging, not the hot path.
+bool debug_validation() {
+  const char* v = std::getenv("PENSIEVE_DEBUG");
+  return v && v[0] == '1' && v[1] == '\0';
+}
+
+hipError_t fetch_i32(std::vector<int32_t>& out, const int32_t* dev, size_t n, hipStream_t stream) {
+  out.assign(n, 0);
+  if (n == 0) return hipSuccess;
+  hipError_t e = hipMemcpyAsync(out.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return e;
+  return hipStreamSynchronize(stream);
+}
+
+pensieve_status validate_slots(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                               hipStream_t stream) {
+  std::vector<int32_t> slots;
+  hipError_t e = fetch_i32(slots, slot_mapping, (size_t)num_tokens, stream);
+  if (e != hipSuccess) return hip_fail(e, "debug validation: reading slot_mapping");
+  const long long limit = (long long)num_blocks * kBlockSize;
+  std::vector<int32_t> used;
+  for (int32_t t = 0; t < num_tokens; ++t) {
+    if (slots[t] < 0) continue;
+    if (slots[t] >= limit)
+      return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: slot_mapping[%d] = %d is past the pool (%lld slots)", t,
+                  slots[t], limit);
+    used.push_back(slots[t]);
+  }
+  std::sort(used.begin(), used.end());
+  for (size_t i = 1; i < used.size(); ++i)
+    if (used[i] == used[i - 1])
+      return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: slot %d appears twice in slot_mapping", used[i]);
+  return PENSIEVE_OK;
+}
+
+pensieve_status validate_batch(const pensieve_batch_desc* d, const int32_t* block_tables, const int32_t* context_lens,
+                               const int32_t* cu_q_lens, const int32_t* q_pos, hipStream_t stream) {
+  const int R = d->num_reqs;
+  const int T = R > 0 ? d->cu_q_lens_host[R] : 0;
+  std::vector<int32_t> bt, ctx, cu, qp;
+  hipError_t e;
+  if ((e = fetch_i32(ctx, context_lens, (size_t)R, stream)) != hipSuccess ||
+      (e = fetch_i32(cu, cu_q_lens, (size_t)R + 1, stream)) != hipSuccess ||
+      (e = fetch_i32(bt, block_tables, (size_t)R * d->block_table_stride, stream)) != hipSuccess ||
+      (q_pos && (e = fetch_i32(qp, q_pos, (size_t)T, stream)) != hipSuccess))
+    return hip_fail(e, "debug validation: reading the batch metadata");
+  for (int r = 0; r < R; ++r)
+    if (ctx[r] != d->context_lens_host[r])
+      return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: context_lens[%d] = %d on the device, %d in the host copy", r,
+                  ctx[r], d->context_lens_host[r]);
+  for (int r = 0; r <= R; ++r)
+    if (cu[r] != d->cu_q_lens_host[r])
+      return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: cu_q_lens[%d] = %d on the device, %d in the host copy", r,
+                  cu[r], d->cu_q_lens_host[r]);
+  for (int r = 0; r < R; ++r) {
+    const int L = ctx[r];
+    const int nblk = (L + kBlockSize - 1) / kBlockSize;
+    for (int j = 0; j < nblk; ++j) {
+      const int32_t b = bt[(size_t)r * d->block_table_stride + j];
+      if (b < 0 || b >= d->num_blocks)
+        return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: block_tables[%d][%d] = %d is outside the pool (%d blocks)",
+                    r, j, b, d->num_blocks);
+    }
+    if (!q_pos) continue;
+    for (int i = cu[r]; i < cu[r + 1]; ++i) {
+      if (qp[i] < 0 || qp[i] >= L)
+        return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: q_pos[%d] = %d is outside [0, %d) of request %d", i, qp[i],
+                    L, r);
+      if (i > cu[r] && qp[i] <= qp[i - 1])
+        return fail(PENSIEVE_ERR_INVALID_ARG, "PENSIEVE_DEBUG: q_pos is not strictly increasing at row %d (request %d)",
+                    i, r);
+    }
+  }
+  return PENSIEVE_OK;
+}
+
 }  // namespace
 
 namespace pk {
@@ -897,6 +980,10 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
     return fail(PENSIEVE_ERR_INVALID_ARG, "a device pointer is NULL");
+  if (debug_validation()) {
+    const pensieve_status s = validate_slots(slot_mapping, num_tokens, num_blocks, static_cast<hipStream_t>(stream));
+    if (s != PENSIEVE_OK) return s;
+  }
   TraceScope trace(kTraceAppend, num_tokens, static_cast<hipStream_t>(stream));
   hipError_t e = pk::launch_kv_append(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads, head_dim,
                                       elem_bytes(dtype), static_cast<hipStream_t>(stream));
@@ -921,6 +1008,10 @@ pensieve_status pensieve_kv_append_fp8(const void* k_new, const void* v_new, voi
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping)
     return fail(PENSIEVE_ERR_INVALID_ARG, "a device pointer is NULL");
+  if (debug_validation()) {
+    const pensieve_status s = validate_slots(slot_mapping, num_tokens, num_blocks, static_cast<hipStream_t>(stream));
+    if (s != PENSIEVE_OK) return s;
+  }
   TraceScope trace(kTraceAppend, num_tokens, static_cast<hipStream_t>(stream));
   hipError_t e = pk::launch_kv_append_fp8(k_new, v_new, k_pool, v_pool, slot_mapping, num_tokens, num_kv_heads,
                                           head_dim, src_dtype, k_scale, v_scale, static_cast<hipStream_t>(stream));
@@ -951,6 +1042,10 @@ pensieve_status pensieve_attn_fwd(const pensieve_batch_desc* desc, const void* q
   if (!o) return fail(PENSIEVE_ERR_INVALID_ARG, "o is NULL");
   if (o == q) return fail(PENSIEVE_ERR_INVALID_ARG, "o must not alias q");
   if ((s = refuse_capture(static_cast<hipStream_t>(stream))) != PENSIEVE_OK) return s;
+  if (debug_validation() &&
+      (s = validate_batch(desc, block_tables, context_lens, cu_q_lens, q_pos, static_cast<hipStream_t>(stream))) !=
+          PENSIEVE_OK)
+    return s;
   thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, 0, plan);
   if (!workspace || workspace_bytes < plan.bytes())
@@ -973,6 +1068,10 @@ pensieve_status pensieve_attn_fwd_noalloc(const pensieve_batch_desc* desc, const
   if (!o) return fail(PENSIEVE_ERR_INVALID_ARG, "o is NULL");
   if (o == q) return fail(PENSIEVE_ERR_INVALID_ARG, "o must not alias q");
   if ((s = refuse_capture(static_cast<hipStream_t>(stream))) != PENSIEVE_OK) return s;
+  if (debug_validation() &&
+      (s = validate_batch(desc, block_tables, context_lens, cu_q_lens, q_pos, static_cast<hipStream_t>(stream))) !=
+          PENSIEVE_OK)
+    return s;
   thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, 0, plan);
   if (plan.bytes() > pk::kScratchBytes)
@@ -1001,6 +1100,10 @@ pensieve_status pensieve_attn_split_partial(const pensieve_batch_desc* desc, int
   if (total_q(desc) == 0) return ok();
   if (!part_o || !part_m || !part_l) return fail(PENSIEVE_ERR_INVALID_ARG, "a partial buffer is NULL");
   if ((s = refuse_capture(static_cast<hipStream_t>(stream))) != PENSIEVE_OK) return s;
+  if (debug_validation() &&
+      (s = validate_batch(desc, block_tables, context_lens, cu_q_lens, q_pos, static_cast<hipStream_t>(stream))) !=
+          PENSIEVE_OK)
+    return s;
   thread_local Plan plan;   // keeps its capacity from call to call
   build_plan(desc, num_partitions, plan);
   if (!workspace || workspace_bytes < plan.bytes())
