@@ -79,7 +79,7 @@ class DeviceBatch:
         self.kv_bytes = 1 if kv_fp8 else b.elem_bytes
         pd = torch.uint8 if kv_fp8 else td
         self.k_pool = torch.empty((b.num_blocks, b.num_kv_heads, 16, b.head_dim), dtype=pd, device="cuda")
-        self.v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.head_dim, 16), dtype=pd, device="cuda")
+        self.v_pool = torch.empty((b.num_blocks, b.num_kv_heads, 16, b.head_dim), dtype=pd, device="cuda")
         if kv_fp8:
             self.k_pool.fill_(0x7F)
             self.v_pool.fill_(0x7F)
@@ -515,7 +515,7 @@ def split_sweep(steps: int = 20, warmup: int = 3):
             bt[r, :nblk[r]] = perm[off:off + nblk[r]]
             off += int(nblk[r])
         kp = torch.randn((NB, heads, 16, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
-        vp = torch.randn((NB, heads, d, 16), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        vp = torch.randn((NB, heads, 16, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
         q = torch.randn((R, heads, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
         o = torch.empty_like(q)
         ctx_d, cu_d = torch.from_numpy(ctx).cuda(), torch.from_numpy(cu).cuda()

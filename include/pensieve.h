@@ -39,7 +39,7 @@
  *     q, o          [total_q][num_heads][head_dim]; rows of request r are
  *                   cu_q_lens[r] .. cu_q_lens[r+1]-1
  *     k_pool        [num_blocks][num_kv_heads][16][head_dim]   (token rows)
- *     v_pool        [num_blocks][num_kv_heads][head_dim][16]   (dim rows)
+ *     v_pool        [num_blocks][num_kv_heads][16][head_dim]   (token rows)
  *     block_tables  [num_reqs][block_table_stride] int32: logical block j
  *                   of request r lives in physical block block_tables[r][j]
  *   Position t of request r is stored at offset t % 16 of physical block
@@ -162,8 +162,8 @@ const char* pensieve_last_error(void);
 /*
  * KV append: for every token t in [0, num_tokens) with slot_mapping[t] >= 0,
  * write k_new[t] into k_pool at block slot/16, offset slot%16 (a [Hkv][d]
- * row set) and v_new[t] into v_pool at the same place (column slot%16 of the
- * block's [d][16] tiles).  A negative slot skips the token.  The copy is
+ * row set) and v_new[t] into v_pool at the same place.  A negative slot
+ * skips the token.  The copy is
  * bit-exact; nothing else in the pools changes.
  *   k_new, v_new  [num_tokens][num_kv_heads][head_dim], dtype elements
  *   slot_mapping  [num_tokens] int32, each < num_blocks*16, no duplicates
@@ -181,7 +181,7 @@ pensieve_status pensieve_kv_append(const void* k_new, const void* v_new, void* k
  * of value / scale (k_scale for K, v_scale for V): the quotient is computed in
  * float32 with correct rounding, magnitudes beyond 448 saturate to +-448, and
  * the rest round to the nearest code, ties to even; NaN stays NaN.  The pools
- * are [num_blocks][Hkv][16][d] and [num_blocks][Hkv][d][16] bytes.  Scales
+ * are [num_blocks][Hkv][16][d] bytes each.  Scales
  * must be finite and > 0 (INVALID_ARG otherwise).  Reading: the pages name
  * FP8 KV storage without a format or a scaling rule; OCP E4M3 with one scale
  * per pool is taken ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3)).
@@ -196,7 +196,7 @@ pensieve_status pensieve_kv_append_fp8(const void* k_new, const void* v_new, voi
  * Pensieve", Methodology and AI Executive Summary: cached KV tokens move
  * between a GPU tier and a CPU tier, swapped ahead of time with transfers
  * pipelined behind computation).  The host tier k_host/v_host has the pools'
- * block layout ([num_host_blocks][Hkv][16][d] and [num_host_blocks][Hkv][d][16])
+ * block layout ([num_host_blocks][Hkv][16][d] each)
  * and must be page-locked host memory mapped for the device (hipHostMalloc,
  * or a pinned torch tensor).  A swap copies n whole blocks, every KV head:
  *   pensieve_kv_swap_out: host block host_blocks[i] = device block device_blocks[i]

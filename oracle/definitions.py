@@ -23,9 +23,8 @@ What it computes (plain definitions, float64, slow on purpose):
   ("PersistentKV: Page-Aware Decode Scheduling ...", section 2, the split of
   one long context into 32 chapters handled in parallel).
 
-Pool layouts (the library's contract):
-  K pool  [num_blocks][Hkv][B][d]   one block = B token rows of d values
-  V pool  [num_blocks][Hkv][d][B]   one block = d rows of B token values
+Pool layout (the library's contract; the same for K and V):
+  K pool, V pool  [num_blocks][Hkv][B][d]   one block = B token rows of d values
 Q and O are [T][Hq][d], rows packed request by request via ``cu_q_lens``.
 Query head h reads KV head ``h // (Hq // Hkv)``.  A row at position p sees
 keys at positions ``t <= p``.
@@ -129,7 +128,7 @@ def append_kv(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: 
             continue
         block, offset = divmod(slot, block_size)
         k_pool[block, :, offset, :] = k_new[t]
-        v_pool[block, :, :, offset] = v_new[t]
+        v_pool[block, :, offset, :] = v_new[t]
 
 
 # ---------------------------------------------------------------------------
@@ -146,7 +145,7 @@ def gather_kv(k_pool, v_pool, block_table_row, context_len: int, kv_head: int, b
     for j in range(n_blocks):
         phys = int(block_table_row[j])
         k_rows.append(to_f64(k_pool[phys, kv_head], dtype))            # [B][d]
-        v_rows.append(to_f64(v_pool[phys, kv_head], dtype).T)          # [d][B] -> [B][d]
+        v_rows.append(to_f64(v_pool[phys, kv_head], dtype))            # [B][d]
     d = k_pool.shape[-1]
     if n_blocks == 0:
         return np.zeros((0, d)), np.zeros((0, d))

@@ -196,12 +196,12 @@ def _shape(t, name: str, shape):
 
 
 def _pool_shapes(k_pool, v_pool, num_blocks=None, hkv=None, d=None):
-    """K pool [NB][Hkv][16][d], V pool [NB][Hkv][d][16]; returns (NB, Hkv, d)."""
+    """K and V pools [NB][Hkv][16][d]; returns (NB, Hkv, d)."""
     if k_pool.dim() != 4 or k_pool.shape[2] != 16:
         raise ValueError(f"k_pool has shape {tuple(k_pool.shape)}, expected [num_blocks][Hkv][16][head_dim]")
     nb, hk, _, dd = k_pool.shape
     _shape(k_pool, "k_pool", (num_blocks, hkv, 16, d))
-    _shape(v_pool, "v_pool", (nb, hk, dd, 16))
+    _shape(v_pool, "v_pool", (nb, hk, 16, dd))
     return int(nb), int(hk), int(dd)
 
 

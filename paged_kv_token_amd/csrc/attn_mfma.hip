@@ -21,9 +21,11 @@
 //   O^T (D x 32 rows)       += V^T_tile . P^T      (D/32 x 4 MFMAs)
 // K rows are read from LDS in the order that swaps bits 2 and 3 of the MFMA
 // row index; then the 8 scores a lane holds for a 16-key step are 8
-// consecutive keys, which is exactly the layout of the P^T operand, and the
-// V^T operand is one 16-byte LDS read of 8 consecutive keys of one dim row
-// (the V pool stores each block as [D][16], so V^T needs no transpose).
+// consecutive keys, which is exactly the layout of the P^T operand.  V tiles
+// are token rows like K ([16][D] per block); each V^T operand (8 consecutive
+// keys of one dim) comes from gfx950's transposing LDS reads:
+// ds_read_b64_tr_b16 gives a lane one dim of 4 keys (two reads per operand),
+// ds_read_b64_tr_b8 one dim of 8 E4M3 codes (one read per operand).
 #include <climits>
 #include <type_traits>
 
@@ -99,31 +101,6 @@ __device__ __forceinline__ int wave_min_i(int x) {
   return x;
 }
 
-// Zero the 16-bit elements e of an 8-element chunk whose key index first + e >= limit.
-__device__ __forceinline__ u32x4 zero_keys_from(u32x4 v, int first, int limit) {
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    uint32_t keep = 0;
-    if (first + 2 * wd < limit) keep |= 0x0000FFFFu;
-    if (first + 2 * wd + 1 < limit) keep |= 0xFFFF0000u;
-    v[wd] &= keep;
-  }
-  return v;
-}
-
-// Zero the bytes e of a 16-byte chunk whose key index first + e >= limit.
-__device__ __forceinline__ u32x4 zero_bytes_from(u32x4 v, int first, int limit) {
-#pragma unroll
-  for (int wd = 0; wd < 4; ++wd) {
-    uint32_t keep = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (first + 4 * wd + b < limit) keep |= 0xFFu << (8 * b);
-    v[wd] &= keep;
-  }
-  return v;
-}
-
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8): wait until at most N vector-memory operations are outstanding, or
 // until every LDS / scalar-memory operation has finished.
@@ -164,10 +141,31 @@ __device__ __forceinline__ float half_swap_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (int)pr[0]), __builtin_bit_cast(float, (int)pr[1]));
 }
 
-// V tiles keep the pool layout in LDS ([16 keys] per dim row, 32 bytes); the two 16-byte
-// halves of dim row d trade places when vswz(d) = 1, so that the 8 or 16 lanes reading one
-// half column from consecutive dim rows hit distinct bank groups.
-__device__ __forceinline__ int vswz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
+// XOR swizzle of the 16-byte chunk slots of V key row t in LDS: chunk c of row t lives in slot
+// c ^ vswz(t).  The transposing reads of one V^T operand take 4 rows (2-byte elements) or 8
+// rows (E4M3) of a few 16-byte chunks each; with these permutations the rows a half-wave (and
+// each 16-lane group) reads fall in distinct banks, for 64 banks of 4 bytes with 32 lanes served
+// per cycle as well as for 32 banks with 16 (derived by enumeration over every read).
+template <int D, bool F8>
+__device__ __forceinline__ int vswz_rows(int t) {
+  if constexpr (!F8) return D == 128 ? 4 * (t & 3) + 2 * ((t >> 1) & 1) : 2 * (t & 3);   // 0,4,10,14 | 0,2,4,6
+  else return D == 128 ? (t & 7) : ((t >> 1) & 3);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+// Transposing LDS reads (gfx950).  Within each group of 16 lanes: tr16 -- the 8-byte loads of
+// lanes 4r .. 4r+3 form row r of a 4 x 16 matrix of 16-bit elements and lane i receives column
+// i (row r's element in its element r); tr8 -- the loads of lanes 2r, 2r+1 form row r of an
+// 8 x 16 byte matrix and lane i receives column i (row r's byte in its byte r).
+__device__ __forceinline__ v4i16 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+}
+__device__ __forceinline__ u32x2 lds_tr8(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)p));
+}
 
 // XOR swizzle of the 16-byte chunk slots of K row r in LDS: chunk c of row r
 // lives in slot c ^ kswz(r).  kswz swaps bits 2 and 3 of r (mod 16), the same
@@ -190,7 +188,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   constexpr int KT = 64;                  // keys per tile (four blocks)
   constexpr int TOKW = 32 / G;            // tokens per wave
   constexpr int KROW = D * EB;            // bytes of one K row (one key)
-  constexpr int VROW = 16 * EB;           // bytes of one V dim row (16 keys)
   constexpr int BLK = 16 * KROW;          // bytes of one block's K (or V) tile
   constexpr int STAGE = 4 * BLK;          // one 64-key tile of K (or V)
   constexpr int NI = BLK / 1024;          // 1 KB LDS-DMA loads per block and tensor
@@ -203,6 +200,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   constexpr int LDS_BYTES = PIPE > OBYTES ? PIPE : OBYTES;
   static_assert(G >= 1 && G <= 32 && (32 % G) == 0, "group size must divide 32");
   static_assert(NI >= 1, "a block tile must fill whole 1 KB loads");
+  static_assert((KT * KCH) % 256 == 0, "the tail zeroing covers whole tiles");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   __shared__ int s_wmax[4];
@@ -260,39 +258,33 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // ---- LDS-DMA tile loads ---------------------------------------------------------------------
   // Wave w loads block w of each tile, K and V, with NI buffer loads of 1 KB each straight into
   // LDS (lane l lands at +16 l).  K stage: row t (0..63) at t * KROW, chunk c in slot
-  // c ^ kswz(t).  V stage: block b at b * BLK as [D][16]; for 2-byte elements the two 16-byte
-  // halves of dim row d are swapped when vswz(d) is set (a dim row of E4M3 codes is one
-  // 16-byte chunk and stays in place).  Source offsets inside a block tile depend only on the
-  // lane: computed once.
-  const const_i32_ptr bt = as_const(a.block_tables) + (size_t)r * a.bt_stride;
+  // c ^ kswz(t).  V stage: the same rows, chunk c in slot c ^ vswz(t).  Source offsets inside a
+  // block tile depend only on the lane: computed once.
   uint32_t koff[NI], voff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int t16 = j * RPI + lane / KCH;
     koff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ kswz_rows<KCH>(t16)) * 16);
-    if constexpr (F8) {
-      voff[j] = (uint32_t)((j * 64 + lane) * 16);
-    } else {
-      const int d = j * 32 + lane / 2;
-      voff[j] = (uint32_t)(d * 32 + ((lane & 1) ^ vswz(d)) * 16);
-    }
+    voff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ vswz_rows<D, F8>(t16)) * 16);
   }
-  // Physical blocks this wave loads for tiles 0..127, held one per lane (lane l: tiles l and
-  // 64 + l) and read with v_readlane, so that no scalar-load latency sits on the per-tile
-  // path; later tiles of very long partitions read the block table with scalar loads.
-  // Past the partition any block of it serves (those keys are masked).
+  // Physical blocks this wave loads, held one per lane in a window of two VGPRs and read with
+  // v_readlane, so that no scalar-load latency sits on the per-tile path: window k holds tiles
+  // 64k .. 64k + 63 (lane l: tile 64k + l) in register k & 1.  Windows 0 and 1 are loaded
+  // here; at tile 64k (k >= 1) the step refills the register of window k - 1, whose last block
+  // was issued two steps earlier, with window k + 1, 62 steps before its first use.  Past the
+  // partition any block of it serves (those keys are masked).
+  const int32_t* const bt_row = a.block_tables + (size_t)r * a.bt_stride;
+  auto window_block = [&](int k) {            // this lane's block of window k
+    const int lb = kb0 + 4 * (64 * k + lane) + w;
+    return bt_row[lb < kb1 ? lb : kb0];
+  };
   int btw0 = 0, btw1 = 0;
   if (kb0 < kb1) {
-    const int lb0 = kb0 + 4 * lane + w, lb1 = kb0 + 4 * (64 + lane) + w;
-    btw0 = a.block_tables[(size_t)r * a.bt_stride + (lb0 < kb1 ? lb0 : kb0)];
-    btw1 = a.block_tables[(size_t)r * a.bt_stride + (lb1 < kb1 ? lb1 : kb0)];
+    btw0 = window_block(0);
+    btw1 = window_block(1);
   }
   auto block_of = [&](int tile) {            // physical block loaded by this wave for `tile`
-    if (tile < 64) return __builtin_amdgcn_readlane(btw0, tile);
-    if (tile < 128) return __builtin_amdgcn_readlane(btw1, tile - 64);
-    int lb = kb0 + 4 * tile + w;
-    lb = (lb < kb1) ? lb : kb0;
-    return bt[lb];
+    return __builtin_amdgcn_readlane((tile & 64) ? btw1 : btw0, tile & 63);
   };
   auto issue = [&](const uint8_t* pool, const uint32_t* offs, int tile, uint8_t* stage) {
     const uint8_t* src = pool + ((size_t)block_of(tile) * Hkv + g) * BLK;
@@ -312,9 +304,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 
   // Per-lane LDS read offsets, fixed for the whole item.  K: the 8 elements of row
   // (32 mb + krow_of_n) at dims 16 ks + 8 h2 live at krd[ks] + 32 KROW mb inside a K stage
-  // (2-byte elements: chunk 2 ks + h2; E4M3: half h2 of chunk ks).  V: keys 8 h2 .. 8 h2 + 7 of
-  // dim row 32 j + n of block ks live at vrd + 32 VROW j + BLK ks inside a V stage
-  // (vswz(32 j + n) = vswz(n)).
+  // (2-byte elements: chunk 2 ks + h2; E4M3: half h2 of chunk ks).  V: lane n + 32 h2 needs
+  // dim 32 j + n of keys 16 ks + 8 h2 .. + 7 (block ks of the tile).  In its 16-lane group
+  // (gm = bit 4 of the lane: dims 16 gm .. 16 gm + 15 of the 32) the transposing read points
+  // the lane at key row 8 h2 + rr (+ 4 for the second read of 2-byte elements) of block ks, at
+  // the 8 bytes that hold dims 32 j + 16 gm + 4 c4 .. + 3 (2-byte; rr = bits 2..3, c4 = bits
+  // 0..1 of the lane) or 32 j + 16 gm + 8 hb .. + 7 (E4M3; rr = bits 1..3, hb = bit 0); the
+  // row's swizzle depends only on rr.  vrd[j] is that address for block 0 and the first read.
   uint32_t krd[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -323,7 +319,32 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     else
       krd[ks] = (uint32_t)(krow_of_n * KROW + (((2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n)) * 16));
   }
-  const uint32_t vrd = F8 ? (uint32_t)(n * VROW + 8 * h2) : (uint32_t)(n * 32 + ((h2 ^ vswz(n)) * 16));
+  uint32_t vrd[MBD];
+  {
+    const int gm = (lane >> 4) & 1;
+    const int rr = F8 ? (lane & 15) >> 1 : (lane & 15) >> 2;
+    const int sw = vswz_rows<D, F8>(rr);
+#pragma unroll
+    for (int j = 0; j < MBD; ++j) {
+      if constexpr (F8) {
+        vrd[j] = (uint32_t)((8 * h2 + rr) * KROW + (((2 * j) | gm) ^ sw) * 16 + (lane & 1) * 8);
+      } else {
+        const int c4 = lane & 3;
+        vrd[j] = (uint32_t)((8 * h2 + rr) * KROW + (((4 * j) | (2 * gm) | (c4 >> 1)) ^ sw) * 16 + (c4 & 1) * 8);
+      }
+    }
+  }
+  // V^T operand of k-step ks (block ks of the tile), dims 32 j .. 32 j + 31.
+  auto v_operand = [&](const uint8_t* vst, int j, int ks) -> vec8 {
+    const uint8_t* p = vst + vrd[j] + ks * BLK;
+    if constexpr (F8) {
+      return MM::from_e4m3(lds_tr8(p));
+    } else {
+      const v4i16 lo = lds_tr16(p), hi = lds_tr16(p + 4 * KROW);
+      const v4i16 both[2] = {lo, hi};
+      return __builtin_bit_cast(vec8, both);
+    }
+  };
   // One 8-element MFMA operand from LDS: 16 bytes as is, or 8 E4M3 codes widened exactly.
   auto operand = [&](const uint8_t* p) -> vec8 {
     if constexpr (F8) return MM::from_e4m3(*reinterpret_cast<const u32x2*>(p));
@@ -384,24 +405,20 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     lds_barrier();
     if (k2) issue(a.k_pool, koff, ti + 2, k_free);
     if (v1) issue(a.v_pool, voff, ti + 1, v_free);
+    if (PAR == 0 && ti >= 64 && (ti & 63) == 0 && ti + 64 < ntiles) {
+      // Refill: window ti / 64 + 1 into the register of window ti / 64 - 1 (same parity).
+      const int nxt = window_block((ti >> 6) + 1);
+      if (ti & 64) btw0 = nxt;
+      else btw1 = nxt;
+    }
     if (t0 + KT > t_valid) {
-      // Tail: keys at or past t_valid must contribute exactly 0; stale V may hold NaN.
+      // Tail: keys at or past t_valid must contribute exactly 0; stale V may hold NaN, so their
+      // whole rows are zeroed in LDS.
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int row = tid + 256 * x;       // (block, dim row) pairs: 4 x D
-        if (row < 4 * D) {
-          const int b = row / D, d = row % D;
-          if constexpr (F8) {
-            u32x4* p = reinterpret_cast<u32x4*>(v_cur + b * BLK + d * VROW);
-            *p = zero_bytes_from(*p, t0 + 16 * b, t_valid);
-          } else {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              u32x4* p = reinterpret_cast<u32x4*>(v_cur + b * BLK + d * 32 + ((hh ^ vswz(d)) * 16));
-              *p = zero_keys_from(*p, t0 + 16 * b + 8 * hh, t_valid);
-            }
-          }
-        }
+      for (int x = 0; x < KT * KCH / 256; ++x) {
+        const int ci = tid + 256 * x;        // (key row, chunk) pairs of the tile
+        const int row = ci / KCH, ch = ci % KCH;
+        if (t0 + row >= t_valid) *reinterpret_cast<u32x4*>(v_cur + row * KROW + ch * 16) = u32x4{0u, 0u, 0u, 0u};
       }
       __builtin_amdgcn_s_waitcnt(lgkmcnt0_imm());
       lds_barrier();
@@ -460,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          vop[jj][ks] = operand(v_cur + vrd + (j0 + jj) * 32 * VROW + ks * BLK);
+          vop[jj][ks] = v_operand(v_cur, j0 + jj, ks);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll

@@ -8,13 +8,14 @@
 // online softmax per query vector in registers and the waves merge through
 // LDS at the end.
 //
-// Per 16-token block a wave issues 16-byte loads that cover the K tile
-// [16][D] and the V tile [D][16] exactly once (64 lanes x 16 B per load), so
-// HBM traffic is the algorithmic K/V bytes.  K: lane l of load i holds dims
-// (l % LPT) * EPC .. +EPC of token i * TPI + l / LPT; the q.k partial sums
-// are reduced over the LPT lanes of a token with DPP row operations.  V: lane
-// l of load j holds tokens (l % CPR) * EPC .. +EPC of dim row j * DPI + l / CPR;
-// the softmax weights reach it through a small per-wave LDS array.
+// Per 16-token block a wave issues 16-byte loads that cover the K tile and the
+// V tile (both [16][D], token rows) exactly once (64 lanes x 16 B per load), so
+// HBM traffic is the algorithmic K/V bytes.  Lane l of load i holds dims
+// (l % LPT) * EPC .. +EPC of token i * TPI + l / LPT, of K and of V alike; the
+// q.k partial sums are reduced over the LPT lanes of a token with DPP row
+// operations, which leaves every one of those lanes holding the token's score,
+// so each lane weights its own V elements with no exchange between lanes.  The
+// lanes holding the same dims of different tokens are summed once per item.
 //
 // Semantics ("Stateful Large Language Model Serving with Pensieve", Abstract:
 // attention of several new tokens over a non-contiguous cache): row i sees
@@ -63,16 +64,12 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   constexpr int QCH = EPC * EQ / 16;    // 16-byte Q chunks matching one K chunk
   constexpr int LPT = D * EB / 16;      // lanes holding one K token row
   constexpr int TPI = 64 / LPT;         // K tokens per load
-  constexpr int KI = 16 / TPI;          // K loads per block
-  constexpr int CPR = EB;               // 16-byte chunks per V dim row (16 tokens)
-  constexpr int DPI = 64 / CPR;         // V dim rows per load
-  constexpr int VI = D / DPI;           // V loads per block
+  constexpr int KI = 16 / TPI;          // K loads (and V loads) per block
   constexpr int NW = 4;
   constexpr size_t TILE = (size_t)16 * D * EB;
   static_assert(KT == DT || KT == kFP8, "stored K / V are the query type or E4M3 codes");
   static_assert(LPT >= 1 && LPT <= 32, "unsupported row width");
 
-  __shared__ __attribute__((aligned(16))) float s_p[NW][NQ][16];
   __shared__ float s_m[NW][NQ];
   __shared__ float s_l[NW][NQ];
   __shared__ float s_acc[NW][NQ][D];
@@ -127,12 +124,12 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   const int kb0 = it.part * per;
   const int kb1 = min(min(kb0 + per, nblk), (pmax >> 4) + 1);
 
-  float m[NQ], l[NQ], acc[NQ][VI];
+  float m[NQ], l[NQ], acc[NQ][EPC];     // acc: this lane's dims dim0 .. dim0 + EPC - 1
 #pragma unroll
   for (int n = 0; n < NQ; ++n) {
     m[n] = -INFINITY; l[n] = 0.f;
 #pragma unroll
-    for (int j = 0; j < VI; ++j) acc[n][j] = 0.f;
+    for (int e = 0; e < EPC; ++e) acc[n][e] = 0.f;
   }
 
   const const_i32_ptr bt = as_const(a.block_tables) + (size_t)r * a.bt_stride;
@@ -143,7 +140,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) kr[i] = tile_load16(kt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
 #pragma unroll
-    for (int j = 0; j < VI; ++j) vr[j] = tile_load16(vt, (uint32_t)TILE, (uint32_t)(j * 64 + lane) * 16u);
+    for (int i = 0; i < KI; ++i) vr[i] = tile_load16(vt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
   };
 
   auto process = [&](int blk, const u32x4* kr, const u32x4* vr) {
@@ -182,6 +179,18 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
         for (int n = 0; n < NQ; ++n) sc[n][i] = (t <= qpos[n]) ? sc[n][i] : -INFINITY;
       }
     }
+    // V elements of this lane's tokens; keys at or past the context length must contribute
+    // exactly 0 (stale slots may hold NaN), so they are selected to 0, not multiplied by 0.
+    const bool zero_tail = base + 16 > L;
+    float vf[KI][EPC];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      unpack16<KT>(vr[i], vf[i]);
+      if (zero_tail && base + i * TPI + lane / LPT >= L) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vf[i][e] = 0.f;
+      }
+    }
 #pragma unroll
     for (int n = 0; n < NQ; ++n) {
       float bm = sc[n][0];
@@ -193,36 +202,17 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
       const float corr = fast_exp2((m[n] - m_use) * c);
       float ps = 0.f;
 #pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[n][e] *= corr;
+#pragma unroll
       for (int i = 0; i < KI; ++i) {
         const float p = fast_exp2((sc[n][i] - m_use) * c);
         ps += p;
-        if (lane % LPT == 0) s_p[w][n][i * TPI + lane / LPT] = p;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[n][e] = fmaf(p, vf[i][e], acc[n][e]);
       }
       l[n] = l[n] * corr + ps;
-#pragma unroll
-      for (int j = 0; j < VI; ++j) acc[n][j] *= corr;
       m[n] = m_new;
     }
-    __builtin_amdgcn_wave_barrier();
-    const int tc = (lane % CPR) * EPC;      // first token of this lane's V chunk
-    const bool zero_tail = base + 16 > L;
-#pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      float vf[EPC];
-      unpack16<KT>(vr[j], vf);
-      if (zero_tail) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) vf[e] = (base + tc + e < L) ? vf[e] : 0.f;
-      }
-#pragma unroll
-      for (int n = 0; n < NQ; ++n) {
-        float s = acc[n][j];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) s = fmaf(s_p[w][n][tc + e], vf[e], s);
-        acc[n][j] = s;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
   };
 
   {
@@ -230,7 +220,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
     // of block b + 2 NW are issued before block b is processed.  Loads past the item's last
     // block fetch that block again (unused, and still in L2), so every step issues the same
     // loads and the compiler's wait counts stay exact.
-    u32x4 ka[KI], va[VI], kb[KI], vb[VI], kc[KI], vc[VI];
+    u32x4 ka[KI], va[KI], kb[KI], vb[KI], kc[KI], vc[KI];
     const int b0 = kb0 + w;
     auto clamp_blk = [&](int b) { return b < kb1 ? b : kb1 - 1; };
     wait_vmem_all();
@@ -256,9 +246,9 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   for (int n = 0; n < NQ; ++n) {
     const float lt = xor_sum_from<LPT>(l[n]);
 #pragma unroll
-    for (int j = 0; j < VI; ++j) {
-      const float v = group_sum<CPR>(acc[n][j]);
-      if (lane % CPR == 0) s_acc[w][n][j * DPI + lane / CPR] = v;
+    for (int e = 0; e < EPC; ++e) {
+      const float v = xor_sum_from<LPT>(acc[n][e]);     // over the lanes holding the same dims
+      if (lane < LPT) s_acc[w][n][dim0 + e] = v;
     }
     if (lane == 0) { s_m[w][n] = m[n]; s_l[w][n] = lt; }
   }

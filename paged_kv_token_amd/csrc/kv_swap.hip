@@ -3,7 +3,7 @@
 // KV tokens ahead of time, with the transfers pipelined behind computation).
 //
 // The host tier has the same block layout as the device pools; a swap copies whole blocks (all
-// KV heads: one contiguous [Hkv][16][D] K run and one [Hkv][D][16] V run per block).  A small
+// KV heads: one contiguous [Hkv][16][D] K run and one V run of the same layout per block).  A small
 // grid of workgroups walks the (block, tensor) copies, each with 16-byte accesses that read or
 // write the host tier directly through its device mapping: a batch of scattered blocks is one
 // launch, and the copy (bound by the host link) leaves most of the GPU to the attention kernels

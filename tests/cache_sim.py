@@ -50,7 +50,7 @@ class OracleBackend:
         self.dtype = dtype
         self.fill = fill
         self.k_pool = np.full((num_blocks, num_kv_heads, BLOCK, head_dim), fill, dtype=sd)
-        self.v_pool = np.full((num_blocks, num_kv_heads, head_dim, BLOCK), fill, dtype=sd)
+        self.v_pool = np.full((num_blocks, num_kv_heads, BLOCK, head_dim), fill, dtype=sd)
 
     def free(self, blocks):
         self.k_pool[blocks] = self.fill
@@ -75,7 +75,7 @@ class GpuBackend:
         self.dtype = dtype
         self.num_blocks = num_blocks
         self.k_pool = torch.full((num_blocks, num_kv_heads, BLOCK, head_dim), self.poison, dtype=td, device="cuda")
-        self.v_pool = torch.full((num_blocks, num_kv_heads, head_dim, BLOCK), self.poison, dtype=td, device="cuda")
+        self.v_pool = torch.full((num_blocks, num_kv_heads, BLOCK, head_dim), self.poison, dtype=td, device="cuda")
 
     def free(self, blocks):
         import torch

@@ -85,7 +85,7 @@ def upload(batch: Batch, *, append_new: bool = True, poison: bool = True, pass_q
     b = batch
     td = torch.uint8 if kv_fp8 is not None else torch_dtype(b.dtype)
     k_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.block_size, b.head_dim), dtype=td, device="cuda")
-    v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.head_dim, b.block_size), dtype=td, device="cuda")
+    v_pool = torch.empty((b.num_blocks, b.num_kv_heads, b.block_size, b.head_dim), dtype=td, device="cuda")
     if kv_fp8 is not None:
         k_pool.fill_(0x7F if poison else 0); v_pool.fill_(0x7F if poison else 0)
     elif poison:

@@ -15,7 +15,7 @@ def poison_fill(dtype: str):
 
 
 def oracle_pools(batch: Batch, impl=oracle, poison=True, include_new=True, kv_fp8=None):
-    """Pools [NB][Hkv][B][d] (K) and [NB][Hkv][d][B] (V) filled through ``impl.append_kv``.
+    """Pools [NB][Hkv][B][d] (K and V) filled through ``impl.append_kv``.
 
     Every slot starts as NaN (poison), then cached history and (optionally)
     the step's new rows are appended.  kv_fp8 = (k_scale, v_scale): the pools
@@ -30,7 +30,7 @@ def oracle_pools(batch: Batch, impl=oracle, poison=True, include_new=True, kv_fp
         enc_k = lambda x: oracle.quantize_e4m3(x, batch.dtype, kv_fp8[0])
         enc_v = lambda x: oracle.quantize_e4m3(x, batch.dtype, kv_fp8[1])
     k_pool = np.full((nb, hkv, B, d), fill, dtype=sd)
-    v_pool = np.full((nb, hkv, d, B), fill, dtype=sd)
+    v_pool = np.full((nb, hkv, B, d), fill, dtype=sd)
     for r, k, v, slots, pos in batch.iter_requests():
         impl.append_kv(k_pool, v_pool, enc_k(k[pos]), enc_v(v[pos]), slots, B)
     if include_new:

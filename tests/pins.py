@@ -54,7 +54,7 @@ def pin_worked_example(impl):
     B, d, hq, hkv = spec["block_size"], spec["head_dim"], spec["num_heads"], spec["num_kv_heads"]
     nb = spec["num_blocks"]
     k_pool = np.full((nb, hkv, B, d), np.nan, dtype=np.float32)
-    v_pool = np.full((nb, hkv, d, B), np.nan, dtype=np.float32)
+    v_pool = np.full((nb, hkv, B, d), np.nan, dtype=np.float32)
     reqs = spec["requests"]
     stride = max(len(r["block_table"]) for r in reqs)
     bt = np.zeros((len(reqs), stride), dtype=np.int32)
@@ -344,13 +344,13 @@ def pin_nan_poison(impl):
 
 
 def pin_append_slots(impl):
-    """Append writes exactly the named slots, in both pool layouts, and skips negative slots."""
+    """Append writes exactly the named slots of both pools and skips negative slots."""
     for dtype in ("f32", "f16", "bf16"):
         sd = storage_dtype(dtype)
         nb, hkv, B, d = 6, 3, 16, 8
         fill = poison_fill(dtype)
         k_pool = np.full((nb, hkv, B, d), fill, dtype=sd)
-        v_pool = np.full((nb, hkv, d, B), fill, dtype=sd)
+        v_pool = np.full((nb, hkv, B, d), fill, dtype=sd)
         rng = np.random.default_rng(3)
         slots = rng.permutation(nb * B)[:40].astype(np.int32)
         slots[[3, 17]] = -1
@@ -368,14 +368,14 @@ def pin_append_slots(impl):
             for g in range(hkv):
                 for c in range(d):
                     assert k_pool[blk, g, off, c].tobytes() == k_new[t, g, c].tobytes()
-                    assert v_pool[blk, g, c, off].tobytes() == v_new[t, g, c].tobytes()
+                    assert v_pool[blk, g, off, c].tobytes() == v_new[t, g, c].tobytes()
         for blk in range(nb):
             for off in range(B):
                 if not written[blk, off]:
                     assert np.all(np.isnan(k_pool[blk, :, off, :].astype(np.float32))) if dtype != "bf16" else \
                         np.all(k_pool[blk, :, off, :] == fill)
-                    assert np.all(np.isnan(v_pool[blk, :, :, off].astype(np.float32))) if dtype != "bf16" else \
-                        np.all(v_pool[blk, :, :, off] == fill)
+                    assert np.all(np.isnan(v_pool[blk, :, off, :].astype(np.float32))) if dtype != "bf16" else \
+                        np.all(v_pool[blk, :, off, :] == fill)
 
 
 ALL_PINS = [

@@ -64,12 +64,12 @@ def test_append_scattered_order_and_skips(dtype):
         k_new, v_new = bf16_bits_from_f32(x[0]), bf16_bits_from_f32(x[1])
     fill = poison_fill(dtype)
     k_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
-    v_ref = np.full((nb, hkv, d, 16), fill, dtype=sd)
+    v_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
     oracle.append_kv(k_ref, v_ref, k_new, v_new, slots, 16)
     _say(f"scattered {dtype}: n={n} nb={nb}")
     from gpu_harness import torch_dtype
     k_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
-    v_pool = poison_(torch.empty((nb, hkv, d, 16), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    v_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
     pk.pensieve_kv_append(to_device(k_new, dtype), to_device(v_new, dtype), k_pool, v_pool,
                           torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
@@ -93,7 +93,7 @@ def test_append_full_size_sampled_blocks(index):
         for j in sorted(set([0, nblk - 1, int(rng.integers(0, nblk))])):
             phys = int(b.block_tables[r, j])
             mk = np.full((1, b.num_kv_heads, 16, b.head_dim), fill, dtype=sd)
-            mv = np.full((1, b.num_kv_heads, b.head_dim, 16), fill, dtype=sd)
+            mv = np.full((1, b.num_kv_heads, 16, b.head_dim), fill, dtype=sd)
             pos = np.arange(16 * j, min(16 * j + 16, int(b.context_lens[r])))
             oracle.append_kv(mk, mv, k[pos], v[pos], (pos % 16).astype(np.int32), 16)
             gk = to_host_storage(gb.k_pool[phys:phys + 1], b.dtype)
@@ -147,11 +147,11 @@ def test_append_runs_across_windows(dtype):
         k_new, v_new = bf16_bits_from_f32(x[0]), bf16_bits_from_f32(x[1])
     fill = poison_fill(dtype)
     k_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
-    v_ref = np.full((nb, hkv, d, 16), fill, dtype=sd)
+    v_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
     oracle.append_kv(k_ref, v_ref, k_new, v_new, slots, 16)
     _say(f"runs {dtype}: n={n} nb={nb}")
     k_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
-    v_pool = poison_(torch.empty((nb, hkv, d, 16), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    v_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
     pk.pensieve_kv_append(to_device(k_new, dtype), to_device(v_new, dtype), k_pool, v_pool,
                           torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()
@@ -199,11 +199,11 @@ def test_append_random_run_layouts(seed):
     k_new, v_new = (x[0].astype(np.float16), x[1].astype(np.float16)) if dtype == "f16" else (x[0], x[1])
     fill = poison_fill(dtype)
     k_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
-    v_ref = np.full((nb, hkv, d, 16), fill, dtype=sd)
+    v_ref = np.full((nb, hkv, 16, d), fill, dtype=sd)
     oracle.append_kv(k_ref, v_ref, k_new, v_new, slots, 16)
     _say(f"random runs seed {seed} {dtype}: n={n}")
     k_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
-    v_pool = poison_(torch.empty((nb, hkv, d, 16), dtype=torch_dtype(dtype), device="cuda"), dtype)
+    v_pool = poison_(torch.empty((nb, hkv, 16, d), dtype=torch_dtype(dtype), device="cuda"), dtype)
     pk.pensieve_kv_append(to_device(k_new, dtype), to_device(v_new, dtype), k_pool, v_pool,
                           torch.from_numpy(slots).cuda())
     torch.cuda.synchronize()

@@ -66,10 +66,10 @@ def test_append_fp8_is_bit_exact(src, d, scale):
     slots[::11] = -1                                             # distinct slots, some skipped
     _say(f"append {src} d={d} scale={scale}: {n} tokens, {int((slots >= 0).sum())} written")
     kp = np.full((nb, hkv, 16, d), 0xAA, np.uint8)
-    vp = np.full((nb, hkv, d, 16), 0xAA, np.uint8)
+    vp = np.full((nb, hkv, 16, d), 0xAA, np.uint8)
     oracle.append_kv(kp, vp, oracle.quantize_e4m3(k, src, scale), oracle.quantize_e4m3(v, src, scale), slots, 16)
     gk = torch.full((nb, hkv, 16, d), 0xAA, dtype=torch.uint8, device="cuda")
-    gv = torch.full((nb, hkv, d, 16), 0xAA, dtype=torch.uint8, device="cuda")
+    gv = torch.full((nb, hkv, 16, d), 0xAA, dtype=torch.uint8, device="cuda")
     pk.pensieve_kv_append_fp8(to_device(k, src), to_device(v, src), gk, gv, torch.from_numpy(slots).cuda(),
                               scale, scale)
     torch.cuda.synchronize()

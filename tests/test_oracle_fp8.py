@@ -122,7 +122,7 @@ def test_fp8_attention_matches_sdpa_over_torch_decoded_kv():
         for h in range(4):
             g = h // 2
             kk = np.concatenate([_torch_decode(kc[p, g]) for p in blocks])[:L] * ks
-            vv = np.concatenate([_torch_decode(vc[p, g]).T for p in blocks])[:L] * vs
+            vv = np.concatenate([_torch_decode(vc[p, g]) for p in blocks])[:L] * vs
             qq = q[lo:hi, h]
             mask = np.arange(L)[None, :] <= np.arange(L - (hi - lo), L)[:, None]
             ref = torch.nn.functional.scaled_dot_product_attention(
@@ -140,7 +140,7 @@ def test_fp8_zero_query_is_the_scaled_mean_of_the_codes():
                                  b.softmax_scale, b.dtype, kv_dtype="e4m3", k_scale=0.05, v_scale=vs)
     blocks = b.block_tables[0][:3]
     for h in range(2):
-        codes = np.concatenate([vc[p, h].T for p in blocks])[:36]
+        codes = np.concatenate([vc[p, h] for p in blocks])[:36]
         vals = np.array([[oracle.e4m3_value(int(c)) for c in row] for row in codes]) * vs
         for i, p in enumerate(range(33, 36)):
             np.testing.assert_allclose(got[i, h], vals[: p + 1].mean(axis=0), rtol=0, atol=1e-14)

@@ -28,11 +28,12 @@ def _gather_swapped(k_pool, v_pool, row, L, g, B, dtype):
     return v, k
 
 
-def _gather_v_untransposed(k_pool, v_pool, row, L, g, B, dtype):
+def _gather_v_dim_major(k_pool, v_pool, row, L, g, B, dtype):
+    """Reads each V block as if it were stored [d][B] (dim rows) instead of [B][d]."""
     n = -(-L // B)
     k, _ = _orig["gather_kv"](k_pool, v_pool, row, L, g, B, dtype)
     d = k_pool.shape[-1]
-    vs = [defs.to_f64(v_pool[int(row[j]), g], dtype).reshape(B, d) for j in range(n)]
+    vs = [defs.to_f64(v_pool[int(row[j]), g], dtype).reshape(d, B).T for j in range(n)]
     return k, np.concatenate(vs)[:L] if vs else np.zeros((0, d))
 
 
@@ -107,7 +108,7 @@ MUTANTS = {
     "gqa_first_head": {"kv_head_of": lambda h, hq, hkv: 0},
     "gather_shifted_blocks": {"gather_kv": _gather_shifted},
     "gather_k_v_swapped": {"gather_kv": _gather_swapped},
-    "gather_v_untransposed": {"gather_kv": _gather_v_untransposed},
+    "gather_v_untransposed": {"gather_kv": _gather_v_dim_major},
     "default_positions_shift": {"default_positions": lambda L, q: np.arange(L - q - 1, L - 1)},
     "q_pos_ignored": {"row_positions": lambda qp, lo, hi, L: np.arange(L - (hi - lo), L)},
     "no_scale": {"causal_attention": _attn_no_scale},
