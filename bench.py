@@ -13,8 +13,17 @@ left in the last-level cache by the step before.
 
 Prints ONE JSON line with the headline metric (query tokens/s), a roofline
 object for the dominant kernel (per-launch durations come from HIP events the
-library records on its launch stream during the timed region), and the CPU
-oracle timed on this host on a bounded sample of the same workload.
+library records on its launch stream during the timed region; average, median
+and shortest sampled launch), and the CPU oracle timed on this host (float32,
+and float64) on a bounded sample of the same workload.
+
+Beside the headline: the other workloads' attention calls, each timed as a
+burst (40 calls after a short warm-up) and sustained (200 calls after 3 s of
+back-to-back calls; their rooflines come from these), the long-context
+workload also with a fixed 32-way split and unsplit, each with the oracle timed
+on a bounded sample; the block swap; and the E4M3-pool lines.  `--only INDEX`
+(with `--fp8`) measures one of these lines alone, exactly as the full run does,
+for profiling runs.
 """
 
 from __future__ import annotations
@@ -139,6 +148,19 @@ class DeviceBatch:
         k_pool, v_pool, q, o = self._next()
         pk.pensieve_attn_fwd(self.desc, q, k_pool, v_pool, self.bt, self.ctx, self.cu, self.q_pos, o, self.ws)
 
+    def attn_no_split(self):
+        """pensieve_attn_fwd with the adaptive split-KV turned off (every request whole)."""
+        if not hasattr(self, "desc_ns"):
+            b = self.b
+            self.desc_ns = pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                                        num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
+                                        dtype={"f32": 0, "f16": 1, "bf16": 2}[b.dtype],
+                                        softmax_scale=b.softmax_scale, context_lens_host=b.context_lens,
+                                        cu_q_lens_host=b.cu_q_lens, flags=pk.PENSIEVE_FLAG_NO_SPLIT,
+                                        q_pos_host=None if b.has_default_positions else b.q_pos)
+        k_pool, v_pool, q, o = self._next()
+        pk.pensieve_attn_fwd(self.desc_ns, q, k_pool, v_pool, self.bt, self.ctx, self.cu, self.q_pos, o, self.ws)
+
     def split_step(self, P, bufs):
         po, pm, pl, ws = bufs
         k_pool, v_pool, q, o = self._next()
@@ -241,17 +263,45 @@ def time_steps(fn, steps: int, warmup: int):
 
 
 def summarize_trace(trace, steps: int):
-    """Per kernel kind: sampled launches, their average duration, and the estimated time per
-    step (each kind's launches are sampled one in TRACE_EVERY)."""
+    """Per kernel kind: sampled launches, their average, median and shortest duration, and the
+    estimated time per step (each kind's launches are sampled one in TRACE_EVERY)."""
     per = {}
     for name, items, ms in trace:
-        d = per.setdefault(name, {"launches": 0, "total_ms": 0.0, "items": items})
+        d = per.setdefault(name, {"launches": 0, "total_ms": 0.0, "items": items, "all": []})
         d["launches"] += 1
         d["total_ms"] += ms
+        d["all"].append(ms)
     for d in per.values():
         d["avg_ms"] = d["total_ms"] / d["launches"]
+        d["median_ms"] = float(np.median(d["all"]))
+        d["min_ms"] = float(np.min(d["all"]))
         d["per_step_ms"] = d["total_ms"] * TRACE_EVERY / steps
+        del d["all"]
     return per
+
+
+def kernel_stats(per):
+    """{kernel: {avg, median, min}} in ms, rounded, for the JSON line."""
+    return {k: {"avg": round(v["avg_ms"], 4), "median": round(v["median_ms"], 4), "min": round(v["min_ms"], 4)}
+            for k, v in per.items()}
+
+
+SUSTAIN_S = 3.0    # seconds of back-to-back calls before a sustained measurement
+
+
+def sustained(fn, steps: int, seconds: float):
+    """Run fn back to back for `seconds` (the GPU settles at the clock it holds under continuous
+    load), then time `steps` more calls as time_steps does."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        fn()
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
+    ms, trace = time_steps(fn, steps, 5)
+    return ms, trace, n
 
 
 def roofline_for(b, dev, per, kernel: str, counters):
@@ -266,21 +316,22 @@ def roofline_for(b, dev, per, kernel: str, counters):
     ridge = MFMA_PEAK_TFLOPS[b.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = None
     if counters:
-        c = counters.get(f"{kernel}@{b.name}") if dev.kv_fp8 is None else None
+        c = counters.get(f"{kernel}@{b.name}" + ("" if dev.kv_fp8 is None else "@fp8"))
         if c and c.get("source_sha") == source_digest(kernel):
             traffic = c.get("traffic_bytes_per_launch")
+    launches = {"avg_launch_ms": round(per[kernel]["avg_ms"], 4), "median_launch_ms": round(per[kernel]["median_ms"], 4),
+                "min_launch_ms": round(per[kernel]["min_ms"], 4), "timed_launches": per[kernel]["launches"],
+                "launch_sampling": f"1 in {TRACE_EVERY}"}
     if intensity < ridge:
         achieved = nbytes / avg_s / 1e9
         return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": nbytes, "algorithmic_flops": flops, "avg_launch_ms": round(per[kernel]["avg_ms"], 4),
-                "timed_launches": per[kernel]["launches"], "launch_sampling": f"1 in {TRACE_EVERY}"}
+                "algorithmic_bytes": nbytes, "algorithmic_flops": flops, **launches}
     achieved = flops / avg_s / 1e12
     peak = MFMA_PEAK_TFLOPS[b.dtype]
     return {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4), "traffic": traffic, "algorithmic_bytes": nbytes,
-            "algorithmic_flops": flops, "avg_launch_ms": round(per[kernel]["avg_ms"], 4),
-            "timed_launches": per[kernel]["launches"], "launch_sampling": f"1 in {TRACE_EVERY}"}
+            "algorithmic_flops": flops, **launches}
 
 
 def load_counters():
@@ -384,16 +435,22 @@ def cpu_model() -> str:
     return "unknown CPU"
 
 
-def cpu_baseline(b, budget_s: float, min_s: float = MIN_CPU_S):
-    """The CPU oracle (as it stands) on this host: all requests, as many query heads as fit the budget."""
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(b, budget_s: float, min_s: float = MIN_CPU_S, compute=np.float32):
+    """The CPU oracle (as it stands) on this host: all requests, as many query heads as fit the budget,
+    carried out in `compute` (float32, the precision the oracle is named in; float64 is the parity
+    oracle's default)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     from oracle_helpers import oracle_pools
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _blas_threads()
     pools = oracle_pools(b)
     q = b.q_all()
     qpos = None if b.has_default_positions else b.q_pos
@@ -407,7 +464,7 @@ def cpu_baseline(b, budget_s: float, min_s: float = MIN_CPU_S):
         heads = list(range(first, min(first + chunk, b.num_heads)))
         t0 = time.perf_counter()
         oracle.paged_attention(q, pools[0], pools[1], b.block_tables, b.context_lens, b.cu_q_lens, qpos,
-                               b.softmax_scale, b.dtype, heads=heads)
+                               b.softmax_scale, b.dtype, heads=heads, compute=compute)
         elapsed += time.perf_counter() - t0
         done += len(heads)
     rate = b.total_q * (done / b.num_heads) / elapsed
@@ -415,8 +472,58 @@ def cpu_baseline(b, budget_s: float, min_s: float = MIN_CPU_S):
         what = f"all {b.num_reqs} requests x all {b.num_heads} query heads, {done / b.num_heads:.2f} passes"
     else:
         what = f"all {b.num_reqs} requests x query heads 0..{done - 1} of {b.num_heads} (rate scaled to all heads)"
+    prec = "float32" if compute == np.float32 else "float64"
     return {"value": round(rate, 2), "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{what} ({elapsed:.1f} s, float64 NumPy on {cpu_model()})"}
+            "sample": f"{what} ({elapsed:.1f} s, {prec} NumPy on {cpu_model()})"}
+
+
+def oracle_sample(b, reqs):
+    """Pools and metadata holding only requests `reqs` of batch b (their own values, blocks renumbered
+    0..n-1 in order), for timing the oracle on a bounded sample of a large workload."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from workloads import storage_dtype
+    nblk = [b.num_logical_blocks(r) for r in reqs]
+    sd = storage_dtype(b.dtype)
+    kp = np.zeros((sum(nblk), b.num_kv_heads, 16, b.head_dim), sd)
+    vp = np.zeros_like(kp)
+    bt = np.zeros((len(reqs), max(nblk)), np.int32)
+    qs, ctx, cu, qpos, off = [], [], [0], [], 0
+    for i, r in enumerate(reqs):
+        bt[i, :nblk[i]] = np.arange(off, off + nblk[i])
+        off += nblk[i]
+        k, v = b.request_kv(r)
+        pos = np.arange(int(b.context_lens[r]))
+        oracle.append_kv(kp, vp, k, v, (bt[i][pos // 16] * 16 + pos % 16).astype(np.int32), 16)
+        qs.append(b.request_q(r))
+        ctx.append(int(b.context_lens[r]))
+        cu.append(cu[-1] + int(b.q_lens[r]))
+        qpos.extend(b.query_positions(r).tolist())
+    return (np.concatenate(qs), kp, vp, bt, np.array(ctx, np.int32), np.array(cu, np.int32),
+            np.array(qpos, np.int32))
+
+
+def cpu_baseline_sample(b, reqs, what: str, budget_s: float, split: int = 0):
+    """The oracle (float32) on requests `reqs` of b, every query head, repeated until budget_s of
+    oracle work; split > 0 times the split pair (partials over `split` partitions, then the merge)."""
+    import oracle
+    q, kp, vp, bt, ctx, cu, qpos = oracle_sample(b, reqs)
+    rows = int(cu[-1])
+    elapsed, passes = 0.0, 0
+    while passes == 0 or elapsed < budget_s:
+        t0 = time.perf_counter()
+        if split:
+            po, pm, pl = oracle.split_partial(q, kp, vp, bt, ctx, cu, qpos, b.softmax_scale, b.dtype, split,
+                                              compute=np.float32)
+            oracle.split_merge(po, pm, pl, compute=np.float32)
+        else:
+            oracle.paged_attention(q, kp, vp, bt, ctx, cu, qpos, b.softmax_scale, b.dtype, compute=np.float32)
+        elapsed += time.perf_counter() - t0
+        passes += 1
+    how = f"split into {split} partitions + merge" if split else "unsplit"
+    return {"value": round(rows * passes / elapsed, 2), "unit": "query-tokens/s", "cores": _blas_threads(),
+            "kind": "oracle", "sample": f"{what}, all {b.num_heads} query heads, {how}: {passes} passes in "
+                                        f"{elapsed:.1f} s (float32 NumPy on {cpu_model()})"}
 
 
 def cpu_single_thread(budget_s: float = 3.0):
@@ -436,40 +543,68 @@ def cpu_single_thread(budget_s: float = 3.0):
     return out
 
 
-def secondary(index: int, steps: int, warmup: int, counters):
-    """Other workloads of the same path, measured the same way (reported beside the headline)."""
+# Bounded oracle samples of the other workloads: (requests, description).
+CPU_SAMPLES = {2: (list(range(8)), "first 8 of 256 decode requests"),
+               3: ([0, 1], "first 2 of 48 requests"),
+               4: ([0, 2], "requests 0 (32768 history, 1 new row) and 2 (49152 history, 512 new rows)")}
+
+
+def secondary(index: int, steps: int, warmup: int, counters, sustain_s: float = SUSTAIN_S, cpu_budget: float = 0.0):
+    """Other workloads of the same path (attention calls alone), reported beside the headline.
+
+    Each is timed twice: a burst of `steps` calls after a short warm-up, and `steps` calls after
+    sustain_s seconds of back-to-back calls (the clock the chip holds under continuous load);
+    the roofline is taken from the sustained calls."""
     import torch
     b = config_batch(index)
     dev = DeviceBatch(b)
     out = {"workload": b.name, "total_q": b.total_q}
-    ms, trace = time_steps(dev.attn, steps, warmup)
+    total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
+    burst = min(steps, BURST_CALLS)
+    ms_b, trace_b = time_steps(dev.attn, burst, warmup)
+    per_b = summarize_trace(trace_b, burst)
+    ms, trace, warm_calls = sustained(dev.attn, steps, sustain_s)
     per = summarize_trace(trace, steps)
     attn = {k: v for k, v in per.items() if k.startswith("attn")}
     dom = max(attn, key=lambda k: attn[k]["total_ms"])
     out["attn_ms"] = round(ms, 4)
     out["query_tokens_per_s"] = round(b.total_q / (ms * 1e-3), 1)
-    out["kernels_ms"] = {k: round(v["avg_ms"], 4) for k, v in per.items()}
+    out["kernels_ms"] = kernel_stats(per)
+    out["timed"] = f"{steps} calls after {warm_calls} back-to-back calls ({sustain_s:g} s)"
     out["roofline"] = roofline_for(b, dev, per, dom, counters)
     # The whole call against HBM: every request's K/V, Q, O and metadata once, over the call's time.
-    total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
     out["attn_hbm_frac"] = round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    out["burst"] = {"timed": f"{burst} calls after {warmup} warm-up calls", "attn_ms": round(ms_b, 4),
+                    "kernels_ms": kernel_stats(per_b),
+                    "roofline_frac": roofline_for(b, dev, per_b, dom, None)["frac"]}
     if index == 4:
         bufs = dev.split_buffers(32)
         ms2, trace2 = time_steps(lambda: dev.split_step(32, bufs), steps, warmup)
         per2 = summarize_trace(trace2, steps)
         out["split32_ms"] = round(ms2, 4)
-        out["split32_kernels_ms"] = {k: round(v["avg_ms"], 4) for k, v in per2.items()}
+        out["split32_kernels_ms"] = kernel_stats(per2)
         out["split32_hbm_frac"] = round(total_bytes / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         del bufs
+        ms3, trace3 = time_steps(dev.attn_no_split, steps, warmup)
+        per3 = summarize_trace(trace3, steps)
+        out["no_split_ms"] = round(ms3, 4)
+        out["no_split_kernels_ms"] = kernel_stats(per3)
+        out["no_split_hbm_frac"] = round(total_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     del dev
     torch.cuda.empty_cache()
+    if cpu_budget > 0 and index in CPU_SAMPLES:
+        reqs, what = CPU_SAMPLES[index]
+        log(f"cpu_baseline (oracle) on {b.name}: {what}")
+        out["cpu_baseline"] = cpu_baseline_sample(b, reqs, what, cpu_budget)
+        if index == 4:
+            out["cpu_baseline_split32"] = cpu_baseline_sample(b, reqs, what, cpu_budget, split=32)
     return out
 
 
 FP8_SCALES = (1 / 128, 1 / 128)   # the workloads' K/V (0.5 N(0,1)) stay below 3, i.e. codes below 384
 
 
-def fp8_measure(index: int, steps: int, warmup: int, full_step: bool):
+def fp8_measure(index: int, steps: int, warmup: int, full_step: bool, counters=None):
     """The same workload with E4M3 pools: whole step (append + attention) or attention alone."""
     import torch
     b = config_batch(index)
@@ -481,8 +616,8 @@ def fp8_measure(index: int, steps: int, warmup: int, full_step: bool):
     out = {"workload": b.name, "kv_dtype": "fp8_e4m3", "scales": list(FP8_SCALES),
            "timed": "step (append + attention)" if full_step else "attention",
            "ms": round(ms, 4), "query_tokens_per_s": round(b.total_q / (ms * 1e-3), 1),
-           "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per.items()},
-           "roofline": roofline_for(b, dev, per, dom, None)}
+           "kernels_ms": kernel_stats(per),
+           "roofline": roofline_for(b, dev, per, dom, counters)}
     attn_ms = sum(v["per_step_ms"] for v in attn.values())
     total_bytes = sum(request_bytes(b, r, 1) for r in range(b.num_reqs))
     out["attn_total"] = {"ms": round(attn_ms, 4), "bytes": total_bytes,
@@ -549,6 +684,43 @@ def split_sweep(steps: int = 20, warmup: int = 3):
     return rows
 
 
+def headline(b, steps: int, warmup: int, counters):
+    """The headline bench line: whole steps (append + attention) on workload b."""
+    import torch
+    dev = DeviceBatch(b)
+    ms, trace = time_steps(dev.step, steps, warmup)
+    per = summarize_trace(trace, steps)
+    dom = max(per, key=lambda k: per[k]["total_ms"])
+    log(f"{ms:.4f} ms/step; kernels (one launch in {TRACE_EVERY} timed): " +
+        ", ".join(f"{k} {v['avg_ms']:.4f} ms x{v['launches'] * TRACE_EVERY / steps:g}" for k, v in per.items()))
+    result = {
+        "metric": METRIC, "value": round(b.total_q / (ms * 1e-3), 1), "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
+        "config": {"workload": b.name, "requests": b.num_reqs, "decode_requests": int((b.new_lens == 1).sum()),
+                   "total_q": b.total_q, "context_tokens": int(b.context_lens.sum()), "num_heads": b.num_heads,
+                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": 16, "seed": b.seed},
+        "roofline": roofline_for(b, dev, per, dom, counters),
+        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per.items()},
+        "kernel_launch_stats_ms": kernel_stats(per),
+    }
+    if "kv_append" in per:
+        ab = append_bytes(b)
+        result["kv_append"] = {"bytes": ab, "avg_ms": round(per["kv_append"]["avg_ms"], 4),
+                               "hbm_frac": round(ab / (per["kv_append"]["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # The attention as a whole (both kernels) against the HBM roofline.
+    attn_ms = sum(v["per_step_ms"] for k, v in per.items() if k.startswith("attn"))
+    total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
+    result["attn_total"] = {"ms": round(attn_ms, 4), "bytes": total_bytes,
+                            "hbm_frac": round(total_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dev
+    torch.cuda.empty_cache()
+    return result
+
+
+BURST_CALLS = 40    # burst figure of the other workloads: the first calls after a short warm-up
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -557,9 +729,18 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="index of the seeded workload to time (default: the "
                     "Llama-2-13B mixed batch); other indices are for profiling runs")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--secondary-cpu-budget", type=float, default=5.0,
+                    help="seconds of oracle work for each other workload's cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-hbm-copy", action="store_true", help="skip the device-copy bandwidth measurement")
+    ap.add_argument("--sustain-s", type=float, default=SUSTAIN_S,
+                    help="seconds of back-to-back calls before the other workloads' sustained measurement")
+    ap.add_argument("--only", type=int, default=None, metavar="INDEX",
+                    help="measure one bench line alone, exactly as the full run does (the headline line for the "
+                         "headline workload, else that workload's secondary line), print it and exit: for "
+                         "profiling runs")
+    ap.add_argument("--fp8", action="store_true", help="with --only: the E4M3-pool line of that workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (a reference kernel for HBM counters)")
     ap.add_argument("--split-sweep", action="store_true",
@@ -589,50 +770,43 @@ def main():
         log(f"calibration copy: {args.copy_calibration} MiB x 2")
         del src, dst
 
+    def fp8_line(idx):
+        head = idx == args.workload
+        return fp8_measure(idx, args.steps if head else BURST_CALLS, args.warmup if head else 5, full_step=head,
+                           counters=counters)
+
+    if args.only is not None:
+        log(f"one bench line: workload {args.only}{' with E4M3 pools' if args.fp8 else ''}")
+        if args.fp8:
+            line = fp8_line(args.only)
+        elif args.only == args.workload:
+            line = headline(config_batch(args.only), args.steps, args.warmup, counters)
+        else:
+            line = secondary(args.only, args.steps, 5, counters, args.sustain_s)
+        print(json.dumps(line), flush=True)
+        return
+
     b = config_batch(args.workload)
     log(f"workload {b.name}: R={b.num_reqs} T={b.total_q} context tokens={int(b.context_lens.sum())}")
-    dev = DeviceBatch(b)
-    ms, trace = time_steps(dev.step, args.steps, args.warmup)
-    per = summarize_trace(trace, args.steps)
-    dom = max(per, key=lambda k: per[k]["total_ms"])
-    log(f"{ms:.4f} ms/step; kernels (one launch in {TRACE_EVERY} timed): " +
-        ", ".join(f"{k} {v['avg_ms']:.4f} ms x{v['launches'] * TRACE_EVERY / args.steps:g}" for k, v in per.items()))
-    roof = roofline_for(b, dev, per, dom, counters)
-    result = {
-        "metric": METRIC, "value": round(b.total_q / (ms * 1e-3), 1), "unit": "query-tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
-        "config": {"workload": b.name, "requests": b.num_reqs, "decode_requests": int((b.new_lens == 1).sum()),
-                   "total_q": b.total_q, "context_tokens": int(b.context_lens.sum()), "num_heads": b.num_heads,
-                   "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": 16, "seed": b.seed},
-        "roofline": roof,
-        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in per.items()},
-    }
-    # The attention as a whole (both kernels) against the HBM roofline.
-    attn_ms = sum(v["per_step_ms"] for k, v in per.items() if k.startswith("attn"))
-    total_bytes = sum(request_bytes(b, r) for r in range(b.num_reqs))
-    result["attn_total"] = {"ms": round(attn_ms, 4), "bytes": total_bytes,
-                            "hbm_frac": round(total_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del dev
-    torch.cuda.empty_cache()
+    result = headline(b, args.steps, args.warmup, counters)
     result["hbm_copy"] = None if args.no_hbm_copy else copy_bandwidth()
     if not args.no_secondary:
         log("block swap with a pinned host tier")
         result["kv_swap"] = swap_measure()
-    if not args.no_secondary:
         result["secondary"] = []
         for idx in (2, 3, 4):
             log(f"secondary workload {idx}")
-            result["secondary"].append(secondary(idx, max(20, args.steps // 4), 5, counters))
-    if not args.no_secondary:
+            result["secondary"].append(secondary(idx, args.steps, 5, counters, args.sustain_s,
+                                                 0.0 if args.no_cpu else args.secondary_cpu_budget))
         result["fp8_kv"] = []
         for idx in (1, 2, 3):
             log(f"fp8 KV pools, workload {idx}")
-            result["fp8_kv"].append(fp8_measure(idx, max(20, args.steps // 4) if idx != 1 else args.steps,
-                                                5 if idx != 1 else args.warmup, full_step=idx == 1))
+            result["fp8_kv"].append(fp8_line(idx))
     if not args.no_cpu:
-        log("cpu_baseline (oracle)")
+        log("cpu_baseline (oracle, float32)")
         result["cpu_baseline"] = cpu_baseline(b, args.cpu_budget)
+        log("cpu_baseline (oracle, float64)")
+        result["cpu_baseline_f64"] = cpu_baseline(b, min(args.cpu_budget, 10.0), compute=np.float64)
         log("oracle on one thread (tiny, 13B mixed and decode-heavy samples)")
         result["cpu_single_thread"] = cpu_single_thread()
     else:

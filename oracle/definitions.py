@@ -4,7 +4,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this module.  The product path never calls it; it
 shares no code, tables or helpers with the HIP library.
 
-What it computes (plain definitions, float64, slow on purpose):
+What it computes (plain definitions, slow on purpose; float64 by default, and float32 on
+request -- the same code with its operands cast, used only to time the oracle as a CPU
+baseline):
 
 * ``append_kv`` -- each new token's K and V rows are copied into the pool
   slot the caller names.  Paging stores KV in fixed-size blocks allocated on
@@ -166,16 +168,17 @@ def causal_visible(key_positions: np.ndarray, row_positions: np.ndarray) -> np.n
 
 def causal_attention(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, positions: np.ndarray,
                      scale: float) -> np.ndarray:
-    """softmax(q k^T * scale, keys t <= position of the row) v, in float64.
+    """softmax(q k^T * scale, keys t <= position of the row) v, in the operands' float type.
 
     q_rows [n][d], k/v [L][d], positions [n] (each < L).  Masked keys get a
     weight of exactly zero.
     """
+    ct = np.result_type(q_rows, k, v, np.float32)
     n = q_rows.shape[0]
-    out = np.zeros((n, v.shape[1]), dtype=np.float64)
+    out = np.zeros((n, v.shape[1]), dtype=ct)
     if n == 0:
         return out
-    scores = (q_rows.astype(np.float64) @ k.T) * float(scale)          # [n][L]
+    scores = (q_rows.astype(ct, copy=False) @ k.T.astype(ct, copy=False)) * ct.type(scale)   # [n][L]
     visible = causal_visible(np.arange(k.shape[0]), positions)         # [n][L]
     masked = np.where(visible, scores, -np.inf)
     row_max = masked.max(axis=1, keepdims=True)
@@ -200,11 +203,12 @@ def paged_attention(q: np.ndarray, k_pool, v_pool, block_tables: np.ndarray,
                     context_lens: np.ndarray, cu_q_lens: np.ndarray, q_pos: Optional[np.ndarray],
                     softmax_scale: float, dtype: str, *, requests: Optional[Iterable[int]] = None,
                     heads: Optional[Iterable[int]] = None, kv_dtype: Optional[str] = None,
-                    k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                    k_scale: float = 1.0, v_scale: float = 1.0, compute=np.float64) -> np.ndarray:
     """O [T][Hq][d] float64 for the unified batch (rows of skipped requests/heads are NaN).
 
     ``dtype`` is the storage type of Q; the pools hold ``kv_dtype`` (default: the
-    same), read back as decoded value times k_scale / v_scale.
+    same), read back as decoded value times k_scale / v_scale.  ``compute`` is the
+    float type the attention is carried out in (the decoded operands are cast to it).
     """
     kv_dtype = dtype if kv_dtype is None else kv_dtype
     T, Hq, d = q.shape
@@ -220,7 +224,9 @@ def paged_attention(q: np.ndarray, k_pool, v_pool, block_tables: np.ndarray,
         for h in head_list:
             g = kv_head_of(h, Hq, Hkv)
             k, v = gather_kv(k_pool, v_pool, block_tables[r], L, g, block_size, kv_dtype, k_scale, v_scale)
-            out[lo:hi, h, :] = causal_attention(to_f64(q[lo:hi, h, :], dtype), k, v, pos, softmax_scale)
+            qr = to_f64(q[lo:hi, h, :], dtype)
+            out[lo:hi, h, :] = causal_attention(qr.astype(compute, copy=False), k.astype(compute, copy=False),
+                                                v.astype(compute, copy=False), pos, softmax_scale)
     return out
 
 
@@ -246,11 +252,12 @@ def partial_attention(q_rows, k, v, positions, scale, start: int, end: int):
     visible keys; a row with no visible key in the range gets m = -inf,
     l = 0, O_p = 0.
     """
+    ct = np.result_type(q_rows, k, v, np.float32)
     n, dv = q_rows.shape[0], v.shape[1]
-    o = np.zeros((n, dv)); m = np.full(n, -np.inf); l = np.zeros(n)
+    o = np.zeros((n, dv), ct); m = np.full(n, -np.inf, ct); l = np.zeros(n, ct)
     if n == 0 or end <= start:
         return o, m, l
-    scores = (q_rows.astype(np.float64) @ k[start:end].T) * float(scale)
+    scores = (q_rows.astype(ct, copy=False) @ k[start:end].T.astype(ct, copy=False)) * ct.type(scale)
     visible = causal_visible(np.arange(start, end), positions)
     any_vis = visible.any(axis=1)
     masked = np.where(visible, scores, -np.inf)
@@ -266,8 +273,10 @@ def partial_attention(q_rows, k, v, positions, scale, start: int, end: int):
 def split_partial(q: np.ndarray, k_pool, v_pool, block_tables, context_lens, cu_q_lens, q_pos,
                   softmax_scale: float, dtype: str, num_partitions: int, *,
                   requests: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None,
-                  kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0):
-    """Partials part_o [T][Hq][P][d], part_m [T][Hq][P], part_l [T][Hq][P] (float64)."""
+                  kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                  compute=np.float64):
+    """Partials part_o [T][Hq][P][d], part_m [T][Hq][P], part_l [T][Hq][P] (float64 arrays; the
+    attention is carried out in ``compute``)."""
     kv_dtype = dtype if kv_dtype is None else kv_dtype
     T, Hq, d = q.shape
     Hkv = k_pool.shape[1]
@@ -286,7 +295,8 @@ def split_partial(q: np.ndarray, k_pool, v_pool, block_tables, context_lens, cu_
         for h in head_list:
             g = kv_head_of(h, Hq, Hkv)
             k, v = gather_kv(k_pool, v_pool, block_tables[r], L, g, block_size, kv_dtype, k_scale, v_scale)
-            qr = to_f64(q[lo:hi, h, :], dtype)
+            k, v = k.astype(compute, copy=False), v.astype(compute, copy=False)
+            qr = to_f64(q[lo:hi, h, :], dtype).astype(compute, copy=False)
             for p_idx, (s, e) in enumerate(ranges):
                 o, m, l = partial_attention(qr, k, v, pos, softmax_scale, s, e)
                 part_o[lo:hi, h, p_idx, :] = o
@@ -295,10 +305,11 @@ def split_partial(q: np.ndarray, k_pool, v_pool, block_tables, context_lens, cu_
     return part_o, part_m, part_l
 
 
-def split_merge(part_o: np.ndarray, part_m: np.ndarray, part_l: np.ndarray) -> np.ndarray:
+def split_merge(part_o: np.ndarray, part_m: np.ndarray, part_l: np.ndarray, compute=np.float64) -> np.ndarray:
     """O = sum_k w_k O_k / sum_k w_k with w_k = l_k exp(m_k - max_k m_k); empty partitions weigh 0."""
-    m = np.asarray(part_m, dtype=np.float64)
-    l = np.asarray(part_l, dtype=np.float64)
+    m = np.asarray(part_m, dtype=compute)
+    l = np.asarray(part_l, dtype=compute)
+    part_o = np.asarray(part_o, dtype=compute)
     live = l > 0
     m_star = np.where(live, m, -np.inf).max(axis=-1, keepdims=True)
     w = np.where(live, l * np.exp(np.where(live, m, 0.0) - np.where(np.isfinite(m_star), m_star, 0.0)), 0.0)
