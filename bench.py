@@ -549,7 +549,8 @@ CPU_SAMPLES = {2: (list(range(8)), "first 8 of 256 decode requests"),
                4: ([0, 2], "requests 0 (32768 history, 1 new row) and 2 (49152 history, 512 new rows)")}
 
 
-def secondary(index: int, steps: int, warmup: int, counters, sustain_s: float = SUSTAIN_S, cpu_budget: float = 0.0):
+def secondary(index: int, steps: int, warmup: int, counters, sustain_s: float = SUSTAIN_S, cpu_budget: float = 0.0,
+              extras: bool = True):
     """Other workloads of the same path (attention calls alone), reported beside the headline.
 
     Each is timed twice: a burst of `steps` calls after a short warm-up, and `steps` calls after
@@ -577,7 +578,7 @@ def secondary(index: int, steps: int, warmup: int, counters, sustain_s: float = 
     out["burst"] = {"timed": f"{burst} calls after {warmup} warm-up calls", "attn_ms": round(ms_b, 4),
                     "kernels_ms": kernel_stats(per_b),
                     "roofline_frac": roofline_for(b, dev, per_b, dom, None)["frac"]}
-    if index == 4:
+    if index == 4 and extras:
         bufs = dev.split_buffers(32)
         ms2, trace2 = time_steps(lambda: dev.split_step(32, bufs), steps, warmup)
         per2 = summarize_trace(trace2, steps)
@@ -738,8 +739,8 @@ def main():
                     help="seconds of back-to-back calls before the other workloads' sustained measurement")
     ap.add_argument("--only", type=int, default=None, metavar="INDEX",
                     help="measure one bench line alone, exactly as the full run does (the headline line for the "
-                         "headline workload, else that workload's secondary line), print it and exit: for "
-                         "profiling runs")
+                         "headline workload, else that workload's secondary line without its extra unsplit and "
+                         "32-way lines), print it and exit: for profiling runs")
     ap.add_argument("--fp8", action="store_true", help="with --only: the E4M3-pool line of that workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device (a reference kernel for HBM counters)")
@@ -782,7 +783,7 @@ def main():
         elif args.only == args.workload:
             line = headline(config_batch(args.only), args.steps, args.warmup, counters)
         else:
-            line = secondary(args.only, args.steps, 5, counters, args.sustain_s)
+            line = secondary(args.only, args.steps, 5, counters, args.sustain_s, extras=False)
         print(json.dumps(line), flush=True)
         return
 
