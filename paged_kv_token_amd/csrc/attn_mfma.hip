@@ -177,6 +177,16 @@ __device__ __forceinline__ int kswz_rows(int r) {
   return ((x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1)) & (KCH - 1);
 }
 
+// XOR swizzle of the 16-byte chunk slots of E4M3 K row t in LDS (rows of D bytes).  A K operand
+// read takes one whole chunk per lane (two k-steps of 8 codes); the 16 rows a 16-lane group
+// reads then fall in distinct banks, and so do the 8 rows of each 8-lane half (enumerated over
+// every read for 64 banks with 16 lanes served per cycle and 32 banks with 8).
+template <int D>
+__device__ __forceinline__ int kswz8_rows(int t) {
+  if constexpr (D == 128) return (t & 3) ^ ((t >> 2) & 1) ^ (((t >> 3) & 1) << 2);
+  else return ((t >> 1) & 1) ^ ((t >> 2) & 1) ^ (((t >> 3) & 1) << 1);
+}
+
 template <int DT, int KVT, int D, int G>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   using MM = Mfma<DT>;
@@ -232,12 +242,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   int pos = -1;
   if (row_valid) pos = a.q_pos ? a.q_pos[qrow] : (L - q_r + it.q_begin + tok);
 
+  // B operand of k-step ks: 8 query elements.  The 16 k-indices of a step may be any 16 dims as
+  // long as the K operand uses the same: for 2-byte pools step ks takes dims 16 ks + 8 h2 .. + 7;
+  // for E4M3 pools the steps come in pairs (2p, 2p + 1) whose lanes h2 take chunk 2p + h2 of the
+  // K row (dims 16 (2p + h2) .. + 15) in one 16-byte read, 8 dims per step.
   vec8 qreg[KS];
   {
     const uint8_t* qp = a.q + (qrow * Hq + h) * (size_t)(D * 2);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qreg[ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(qp + (ks * 16 + 8 * h2) * 2));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int dim = F8 ? 16 * ((ks & ~1) + h2) + 8 * (ks & 1) : ks * 16 + 8 * h2;
+      qreg[ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(qp + dim * 2));
+    }
   }
   const int pmax_w = uniform(wave_max_i(pos));
   const int pmin_w = uniform(wave_min_i(row_valid ? pos : INT_MAX));   // over valid rows only
@@ -264,7 +280,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int t16 = j * RPI + lane / KCH;
-    koff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ kswz_rows<KCH>(t16)) * 16);
+    const int ksw = F8 ? kswz8_rows<D>(t16) : kswz_rows<KCH>(t16);
+    koff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ ksw) * 16);
     voff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ vswz_rows<D, F8>(t16)) * 16);
   }
   // Physical blocks this wave loads, held one per lane in a window of two VGPRs and read with
@@ -302,9 +319,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // LDS row of the K key that MFMA row (32 mb + n) multiplies: bits 2 and 3 swapped.
   const int krow_of_n = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
 
-  // Per-lane LDS read offsets, fixed for the whole item.  K: the 8 elements of row
-  // (32 mb + krow_of_n) at dims 16 ks + 8 h2 live at krd[ks] + 32 KROW mb inside a K stage
-  // (2-byte elements: chunk 2 ks + h2; E4M3: half h2 of chunk ks).  V: lane n + 32 h2 needs
+  // Per-lane LDS read offsets, fixed for the whole item.  K: the elements of row
+  // (32 mb + krow_of_n) for k-step ks live at krd[ks] + 32 KROW mb inside a K stage (2-byte
+  // elements: chunk 2 ks + h2; E4M3: chunk ks + h2 for even ks, read whole for steps ks, ks + 1).  V: lane n + 32 h2 needs
   // dim 32 j + n of keys 16 ks + 8 h2 .. + 7 (block ks of the tile).  In its 16-lane group
   // (gm = bit 4 of the lane: dims 16 gm .. 16 gm + 15 of the 32) the transposing read points
   // the lane at key row 8 h2 + rr (+ 4 for the second read of 2-byte elements) of block ks, at
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if constexpr (F8)
-      krd[ks] = (uint32_t)(krow_of_n * KROW + ((ks ^ kswz_rows<KCH>(krow_of_n)) * 16) + 8 * h2);
+      krd[ks] = (uint32_t)(krow_of_n * KROW + ((((ks & ~1) + h2) ^ kswz8_rows<D>(krow_of_n)) * 16));
     else
       krd[ks] = (uint32_t)(krow_of_n * KROW + (((2 * ks + h2) ^ kswz_rows<KCH>(krow_of_n)) * 16));
   }
@@ -345,11 +362,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       return __builtin_bit_cast(vec8, both);
     }
   };
-  // One 8-element MFMA operand from LDS: 16 bytes as is, or 8 E4M3 codes widened exactly.
-  auto operand = [&](const uint8_t* p) -> vec8 {
-    if constexpr (F8) return MM::from_e4m3(*reinterpret_cast<const u32x2*>(p));
-    else return __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(p));
-  };
+  // One 8-element K operand of 2-byte elements from LDS (E4M3 rows are read two steps at a time
+  // and widened exactly in qk below).
+  auto operand = [&](const uint8_t* p) -> vec8 { return __builtin_bit_cast(vec8, *reinterpret_cast<const u32x4*>(p)); };
 
   // S^T of one tile for this lane's row: s[mb][v] is key t0 + 32 mb + 16 (v / 8) + 8 h2 + v % 8.
   // K operands are read in batches of four k-steps for both 32-key halves, and the two
@@ -360,11 +375,22 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += 4) {
       vec8 kop[4][2];
+      if constexpr (F8) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; kk += 2)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          kop[kk][mb] = operand(ks_base + krd[k0 + kk] + mb * 32 * KROW);
+          for (int mb = 0; mb < 2; ++mb) {
+            const u32x4 w16 = *reinterpret_cast<const u32x4*>(ks_base + krd[k0 + kk] + mb * 32 * KROW);
+            kop[kk][mb] = MM::from_e4m3(u32x2{w16[0], w16[1]});
+            kop[kk + 1][mb] = MM::from_e4m3(u32x2{w16[2], w16[3]});
+          }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            kop[kk][mb] = operand(ks_base + krd[k0 + kk] + mb * 32 * KROW);
+      }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
