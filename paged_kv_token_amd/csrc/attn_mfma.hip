@@ -116,13 +116,18 @@ constexpr int lgkmcnt0_imm() { return 63 | (3 << 14) | (7 << 4); }
 // so that the compiler's wait-count tracking, which cannot tell one LDS stage from another,
 // does not wait for these loads before every LDS read; callers wait for them explicitly
 // with s_waitcnt vmcnt.  M0 carries the LDS address, bound as an input operand, so the
-// compiler itself writes it and knows it holds that value.
+// compiler itself writes it and knows it holds that value.  NT: the non-temporal form, for
+// K/V that no other workgroup of the launch reads.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t nbytes, uint32_t voff, uint8_t* lds_dst) {
   const unsigned long long b = (unsigned long long)base;
   const i32x4 rsrc = {(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)nbytes, kBufferWord3};
   const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)lds_dst);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+  if constexpr (NT)
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
 }
 
 // Workgroup barrier that does not wait for outstanding memory operations (LDS-DMA
@@ -303,10 +308,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   auto block_of = [&](int tile) {            // physical block loaded by this wave for `tile`
     return __builtin_amdgcn_readlane((tile & 64) ? btw1 : btw0, tile & 63);
   };
+  // When the request's rows fit one item, no other item reads this KV head's tiles of the
+  // partition and the loads are non-temporal; otherwise the items of the request's other rows
+  // read the same tiles at about the same time, through L2.
+  const bool read_once = uniform(q_r <= 4 * TOKW ? 1 : 0) != 0;
   auto issue = [&](const uint8_t* pool, const uint32_t* offs, int tile, uint8_t* stage) {
     const uint8_t* src = pool + ((size_t)block_of(tile) * Hkv + g) * BLK;
+    if (read_once) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j) lds_dma16(src, BLK, offs[j], stage + w * BLK + j * 1024);
+      for (int j = 0; j < NI; ++j) lds_dma16<true>(src, BLK, offs[j], stage + w * BLK + j * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NI; ++j) lds_dma16<false>(src, BLK, offs[j], stage + w * BLK + j * 1024);
+    }
   };
   auto kstage = [&](int tile) { return lds + (tile & 1) * STAGE; };
   auto vstage = [&](int tile) { return lds + (2 + (tile & 1)) * STAGE; };

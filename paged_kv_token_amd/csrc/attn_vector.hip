@@ -133,14 +133,24 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   }
 
   const const_i32_ptr bt = as_const(a.block_tables) + (size_t)r * a.bt_stride;
+  // An item holding every row and query head of its request and KV head is the only reader of
+  // its K/V: those loads are non-temporal.
+  const bool read_once = uniform(hc == G && it.q_count == q_r ? 1 : 0) != 0;
   auto load = [&](int blk, u32x4* kr, u32x4* vr) {
     const int phys = bt[uniform(blk)];
     const uint8_t* kt = a.k_pool + ((size_t)phys * Hkv + g) * TILE;
     const uint8_t* vt = a.v_pool + ((size_t)phys * Hkv + g) * TILE;
+    if (read_once) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i) kr[i] = tile_load16(kt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
+      for (int i = 0; i < KI; ++i) kr[i] = tile_load16<true>(kt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
 #pragma unroll
-    for (int i = 0; i < KI; ++i) vr[i] = tile_load16(vt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
+      for (int i = 0; i < KI; ++i) vr[i] = tile_load16<true>(vt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KI; ++i) kr[i] = tile_load16(kt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
+#pragma unroll
+      for (int i = 0; i < KI; ++i) vr[i] = tile_load16(vt, (uint32_t)TILE, (uint32_t)(i * 64 + lane) * 16u);
+    }
   };
 
   auto process = [&](int blk, const u32x4* kr, const u32x4* vr) {
