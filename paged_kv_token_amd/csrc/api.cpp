@@ -538,20 +538,6 @@ hipError_t stage_release(Stager::Slot* slot, hipStream_t stream) {
   return hipSuccess;
 }
 
-hipError_t stage_to_device(void* dst, const void* src, size_t bytes, hipStream_t stream) {
-  if (bytes == 0) return hipSuccess;
-  void* mapped = nullptr;
-  Stager::Slot* slot = nullptr;
-  hipError_t e = stage_acquire(src, bytes, &mapped, &slot);
-  if (e != hipSuccess) return e;
-  if (bytes % 16 == 0)
-    e = pk::launch_stage_copy(mapped, dst, bytes, stream);
-  else
-    e = hipMemcpyAsync(dst, slot->host, bytes, hipMemcpyHostToDevice, stream);
-  const hipError_t e2 = stage_release(slot, stream);   // gives the slot back even after a failed launch
-  return e != hipSuccess ? e : e2;
-}
-
 // How a plan's work list reaches the device.
 enum class Upload {
   kStaged,     // the pinned staging ring (allocated by the library on first use) and a copy kernel
@@ -688,13 +674,35 @@ int device_cu_count() {
   return n;
 }
 
+// A work list in a staging buffer: the buffer is given back (its reuse guarded by an event on the
+// caller's stream) after the call's last launch, on every return path.
+struct StagedList {
+  Stager::Slot* slot = nullptr;
+  hipStream_t stream = nullptr;
+  hipError_t release() {
+    if (!slot) return hipSuccess;
+    Stager::Slot* s = slot;
+    slot = nullptr;
+    return stage_release(s, stream);
+  }
+  ~StagedList() { (void)release(); }
+};
+
 pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::AttnArgs& args, void* workspace,
                          hipStream_t stream, Upload upload = Upload::kStaged) {
   uint8_t* const ws = static_cast<uint8_t*>(workspace);
+  StagedList staged;
+  staged.stream = stream;
+  const uint8_t* const meta_dev = ws;   // the work list as the kernels read it
   auto to_device = [&](const void* src, size_t bytes) -> hipError_t {
-    if (upload == Upload::kStaged) return stage_to_device(ws, src, bytes, stream);
-    // Pageable source: the copy has taken the bytes when the call returns.
-    return bytes ? hipMemcpyAsync(ws, src, bytes, hipMemcpyHostToDevice, stream) : hipSuccess;
+    if (bytes == 0) return hipSuccess;
+    if (upload == Upload::kPageable)   // pageable source: the copy has taken the bytes when the call returns
+      return hipMemcpyAsync(ws, src, bytes, hipMemcpyHostToDevice, stream);
+    void* mapped = nullptr;
+    hipError_t e = stage_acquire(src, bytes, &mapped, &staged.slot);
+    if (e != hipSuccess) return e;
+    if (bytes % 16 == 0) return pk::launch_stage_copy(mapped, ws, bytes, stream);
+    return hipMemcpyAsync(ws, staged.slot->host, bytes, hipMemcpyHostToDevice, stream);
   };
   hipError_t e;
   if (plan.split_rows == 0) {
@@ -707,14 +715,14 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     std::memcpy(meta.data() + plan.base_off(), plan.part_row_base.data(), plan.part_row_base.size() * sizeof(int32_t));
     std::memcpy(meta.data() + plan.rowmap_off(), plan.rowmap.data(), plan.rowmap.size() * sizeof(int32_t));
     e = to_device(meta.data(), meta.size());
-    args.part_row_base = reinterpret_cast<const int32_t*>(ws + plan.base_off());
+    args.part_row_base = reinterpret_cast<const int32_t*>(meta_dev + plan.base_off());
     args.part_m = reinterpret_cast<float*>(ws + plan.pm_off());
     args.part_l = reinterpret_cast<float*>(ws + plan.pl_off());
     args.part_o = reinterpret_cast<float*>(ws + plan.po_off());
     args.part_stride = plan.pmax;
   }
   if (e != hipSuccess) return hip_fail(e, "work-list upload");
-  const pk::WorkItem* dev_items = reinterpret_cast<const pk::WorkItem*>(ws);
+  const pk::WorkItem* dev_items = reinterpret_cast<const pk::WorkItem*>(meta_dev);
   bool has_matrix = false, has_vector = false;
   for (const Segment& s : plan.segments) (s.kernel == kMatrix ? has_matrix : has_vector) = true;
   Concurrency* conc = nullptr;
@@ -754,9 +762,10 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     const int rows = plan.split_rows * d->num_heads;
     TraceScope trace(kTraceMerge, rows, stream);
     e = pk::launch_split_merge(args.part_o, args.part_m, args.part_l, rows, d->num_heads, d->head_dim, plan.pmax,
-                               reinterpret_cast<const int32_t*>(ws + plan.rowmap_off()), d->dtype, args.o, stream);
+                               reinterpret_cast<const int32_t*>(meta_dev + plan.rowmap_off()), d->dtype, args.o, stream);
     if (e != hipSuccess) return hip_fail(e, "split merge launch");
   }
+  if ((e = staged.release()) != hipSuccess) return hip_fail(e, "staging buffer release");
   return ok();
 }
 

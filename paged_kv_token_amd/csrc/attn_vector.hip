@@ -88,11 +88,14 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
   const float c = a.scale_log2;
 
   // ---- query vectors and their positions -----------------------------------
-  // Float pools: the lane's query elements as floats.  E4M3 pools: kept packed (two elements
-  // per register) and multiplied with the widened codes by two-element dot products.
+  // fp32 pools: the lane's query elements as floats.  f16 / bf16 and E4M3 pools: kept packed
+  // (two elements per register) and multiplied with the stored (or widened) K pairs by
+  // two-element dot products with fp32 accumulation; the products of two 16-bit floats are
+  // exact in fp32.
   constexpr bool F8 = KT == kFP8;
-  float qv[NQ][F8 ? 1 : EPC];
-  uint32_t qh[NQ][F8 ? EPC / 2 : 1];
+  constexpr bool PK = KT != kF32;       // packed query pairs
+  float qv[NQ][PK ? 1 : EPC];
+  uint32_t qh[NQ][PK ? EPC / 2 : 1];
   int qpos[NQ];
   int pmin = 0x7fffffff, pmax = -1;
   const int dim0 = (lane % LPT) * EPC;
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
 #pragma unroll
     for (int qc = 0; qc < QCH; ++qc) {
       const u32x4 qw = *reinterpret_cast<const u32x4*>(a.q + (((size_t)row * Hq + h) * D + dim0) * EQ + qc * 16);
-      if constexpr (F8) {
+      if constexpr (PK) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) qh[n][4 * qc + e] = qw[e];
       } else {
@@ -167,6 +170,14 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(const AttnArgs a) {
           float s = 0.f;
 #pragma unroll
           for (int e = 0; e < EPC / 2; ++e) s = dot2_acc<DT>(qh[n][e], kp[e], s);
+          sc[n][i] = group_sum<LPT>(s);
+        }
+      } else if constexpr (PK) {
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPC / 2; ++e) s = dot2_acc<DT>(qh[n][e], kr[i][e], s);
           sc[n][i] = group_sum<LPT>(s);
         }
       } else {
