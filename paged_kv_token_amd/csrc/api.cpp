@@ -526,14 +526,15 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   return hipSuccess;
 }
 
-// The staging buffer may be reused once the stream has passed this point.
-hipError_t stage_release(Stager::Slot* slot, hipStream_t stream) {
+// The staging buffer may be reused once `stream` has passed this point, or, when the slot's event
+// is already attached to the launch that read the buffer (`recorded`), once that launch is done.
+hipError_t stage_release(Stager::Slot* slot, hipStream_t stream, bool recorded = false) {
   hipError_t e;
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
   std::lock_guard<std::mutex> lk(st->mu);
   slot->in_use = false;
-  if ((e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
+  if (!recorded && (e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
   slot->pending = true;
   return hipSuccess;
 }
@@ -674,16 +675,18 @@ int device_cu_count() {
   return n;
 }
 
-// A work list in a staging buffer: the buffer is given back (its reuse guarded by an event on the
-// caller's stream) after the call's last launch, on every return path.
+// A work list in a staging buffer, given back after the call's last launch on every return path.
+// Its reuse waits for the slot's event: recorded by the copy kernel's own completion when the
+// copy was launched (`attached`), else on the caller's stream at the release.
 struct StagedList {
   Stager::Slot* slot = nullptr;
   hipStream_t stream = nullptr;
+  bool attached = false;
   hipError_t release() {
     if (!slot) return hipSuccess;
     Stager::Slot* s = slot;
     slot = nullptr;
-    return stage_release(s, stream);
+    return stage_release(s, stream, attached);
   }
   ~StagedList() { (void)release(); }
 };
@@ -701,7 +704,11 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     void* mapped = nullptr;
     hipError_t e = stage_acquire(src, bytes, &mapped, &staged.slot);
     if (e != hipSuccess) return e;
-    if (bytes % 16 == 0) return pk::launch_stage_copy(mapped, ws, bytes, stream);
+    if (bytes % 16 == 0) {
+      e = pk::launch_stage_copy(mapped, ws, bytes, stream, staged.slot->ev);
+      staged.attached = e == hipSuccess;
+      return e;
+    }
     return hipMemcpyAsync(ws, staged.slot->host, bytes, hipMemcpyHostToDevice, stream);
   };
   hipError_t e;

@@ -53,11 +53,10 @@ hipError_t launch_kv_swap(const void* src_k, const void* src_v, void* dst_k, voi
                           int n, int64_t block_bytes, hipStream_t stream);
 
 // Copy `bytes` (a multiple of 16) from a device-mapped page-locked host buffer to device
-// memory with a kernel on `stream`.
-hipError_t launch_stage_copy(const void* src_mapped, void* dst, size_t bytes, hipStream_t stream);
+// memory with a kernel on `stream`; `done` (nullable) is recorded by the copy's completion.
+hipError_t launch_stage_copy(const void* src_mapped, void* dst, size_t bytes, hipStream_t stream,
+                             hipEvent_t done = nullptr);
 
-// Merge of split partials into O: rows = partial rows x num_heads; rowmap
-// (nullable) gives each partial row's output row and partition count.
 // Size of the library-owned device scratch of pensieve_attn_fwd_noalloc (one array per GPU).
 constexpr size_t kScratchBytes = (size_t)64 << 20;
 
@@ -65,6 +64,8 @@ constexpr size_t kScratchBytes = (size_t)64 << 20;
 // current, and kept).
 hipError_t scratch_for_current_device(void** ptr);
 
+// Merge of split partials into O: rows = partial rows x num_heads; rowmap
+// (nullable) gives each partial row's output row and partition count.
 hipError_t launch_split_merge(const float* part_o, const float* part_m, const float* part_l, int rows, int num_heads,
                               int head_dim, int num_partitions, const int32_t* rowmap, int dtype, void* o,
                               hipStream_t stream);
