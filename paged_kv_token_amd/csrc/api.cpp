@@ -221,10 +221,14 @@ void sort_descending(std::vector<int>& idx, Key key) {
   idx.swap(tmp);
 }
 
-// Cost class of a work item: the octave of its length in 64-unit steps, floor(log2(cost / 64)).
+// Cost class of a work item: three octaves of its length in 64-unit steps,
+// floor(log2(cost / 64) / 3).  Narrower classes (one octave) spread a request's items over more
+// classes, which run apart in time, so its K/V was fetched again: on the GQA recompute batch the
+// matrix-core launch read 717 MB instead of 606 MB and took 1 % longer; wider ones (four and five
+// octaves) leave longer items in each bin's last round (3-4 % slower).
 int cost_class(long long cost) {
   const unsigned long long steps = (unsigned long long)std::max(1LL, cost / 64);
-  return 63 - __builtin_clzll(steps);
+  return (63 - __builtin_clzll(steps)) / 3;
 }
 
 void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGroup>& groups,
@@ -250,7 +254,7 @@ void xcd_order(const std::vector<PlannedItem>& items, const std::vector<ItemGrou
     load[x] += groups[gi].cost;
     for (int k = 0; k < groups[gi].count; ++k) bins[x].push_back(groups[gi].first + k);
   }
-  // Each XCD runs its items by cost class, longest octave first (items of a request differ when
+  // Each XCD runs its items by cost class, longest class first (items of a request differ when
   // its rows sit at very different positions, e.g. recomputed leading rows), so that its last
   // round holds its shortest items.  Inside a class the items keep the order above, a request's
   // items next to each other, so that they run close together in time and share its K/V in the

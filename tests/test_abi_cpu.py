@@ -111,8 +111,8 @@ def _coverage(b, plan, P=None):
 
 
 def _cost_class(cost) -> int:
-    """Octave of a planned item's cost in 64-unit steps."""
-    return int(max(1, int(cost) // 64)).bit_length() - 1
+    """Class of a planned item's cost: its octave in 64-unit steps, three octaves per class."""
+    return (int(max(1, int(cost) // 64)).bit_length() - 1) // 3
 
 
 @pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
@@ -124,8 +124,8 @@ def test_plan_covers_each_row_head_once(lib, index):
     mat = plan[plan[:, 0] == 1]
     if len(mat) >= 16:
         # matrix-core items: interleaved over 8 XCD bins (slot % 8); each bin runs its items by cost
-        # class (octave of the cost), longest first, and keeps all items of one (request, KV head,
-        # partition) on one XCD
+        # class (three octaves of the cost), longest first, and keeps all items of one (request, KV
+        # head, partition) on one XCD
         assert len(mat) % 8 == 0
         owner = {}
         for x in range(8):
