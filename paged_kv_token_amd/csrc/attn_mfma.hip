@@ -530,7 +530,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     // reads are also placed: six K reads (and twelve transposing V reads, six V^T operands) are
     // issued before the first MFMA of their phase and one more (two) after each MFMA, so every
     // MFMA finds its operand loaded several MFMAs earlier (253 VGPRs, no spills; 2-3 % on the
-    // long-context and GQA recompute batches; eight and sixteen ahead spill).  E4M3 tiles keep
+    // long-context and GQA recompute batches; eight and sixteen ahead spill), and the QK phase
+    // takes two VALU instructions per MFMA (1 % on the long-context batch).  E4M3 tiles keep
     // the scheduler's order: their operand widening adds four VALU conversions per MFMA, and the
     // same pattern made them slower.
     constexpr int KA = 6, VA = 12;           // K and V reads issued ahead of their MFMAs
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       for (int i = 0; i < 2 * KS; ++i) {                       // QK of the next tile
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
         if (i < 2 * KS - KA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // three VALU instructions
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);     // two VALU instructions
       }
       __builtin_amdgcn_sched_group_barrier(0x100, VA, 0);
 #pragma unroll
