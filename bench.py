@@ -685,6 +685,50 @@ def split_sweep(steps: int = 20, warmup: int = 3):
     return rows
 
 
+def routing_sweep(steps: int = 20, warmup: int = 3):
+    """Decode rows of GQA groups on the two kernels: 128 decode requests of 2048 history tokens, 8
+    KV heads of 1, 2, 4 or 8 query heads each, d = 128, bf16 (timing only: pools hold device-side
+    random values).  pensieve_attn_fwd's default routing (the matrix cores from groups of 4) against
+    PENSIEVE_FLAG_VECTOR_ONLY; K/V bytes over time as TB/s."""
+    import torch
+    R, hist, hkv, d = 128, 2048, 8, 128
+    rows = []
+    for G in (1, 2, 4, 8):
+        heads = hkv * G
+        ctx = np.full(R, hist + 1, dtype=np.int32)
+        cu = np.arange(R + 1, dtype=np.int32)
+        nblk = -(-ctx // 16)
+        NB = int(nblk.sum())
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        perm = torch.randperm(NB, device="cuda", generator=gen).to(torch.int32)
+        stride = int(nblk.max())
+        bt = perm.reshape(R, stride).contiguous()
+        kp = torch.randn((NB, hkv, 16, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        vp = torch.randn((NB, hkv, 16, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        q = torch.randn((R, heads, d), device="cuda", dtype=torch.bfloat16, generator=gen) * 0.5
+        o = torch.empty_like(q)
+        ctx_d, cu_d = torch.from_numpy(ctx).cuda(), torch.from_numpy(cu).cuda()
+        mk = lambda flags: pk.make_desc(num_heads=heads, num_kv_heads=hkv, head_dim=d, num_blocks=NB,
+                                        block_table_stride=stride, dtype=pk.PENSIEVE_BF16,
+                                        softmax_scale=1 / math.sqrt(d), context_lens_host=ctx, cu_q_lens_host=cu,
+                                        flags=flags | pk.PENSIEVE_FLAG_NO_SPLIT)
+        d_def, d_vec = mk(0), mk(pk.PENSIEVE_FLAG_VECTOR_ONLY)
+        ws = torch.empty(max(pk.pensieve_attn_workspace_size(d_def), pk.pensieve_attn_workspace_size(d_vec), 256),
+                         dtype=torch.uint8, device="cuda")
+        kernel = "matrix" if any(int(x[0]) == 1 for x in pk.pensieve_debug_plan(d_def)) else "vector"
+        t_def, _ = time_steps(lambda: pk.pensieve_attn_fwd(d_def, q, kp, vp, bt, ctx_d, cu_d, None, o, ws), steps, warmup)
+        t_vec, _ = time_steps(lambda: pk.pensieve_attn_fwd(d_vec, q, kp, vp, bt, ctx_d, cu_d, None, o, ws), steps, warmup)
+        kv = 2 * int(ctx.sum()) * hkv * d * 2
+        row = {"group": G, "default_kernel": kernel, "default_ms": round(t_def, 4),
+               "default_tbs": round(kv / (t_def * 1e-3) / 1e12, 2), "vector_only_ms": round(t_vec, 4),
+               "vector_only_tbs": round(kv / (t_vec * 1e-3) / 1e12, 2)}
+        log(json.dumps(row))
+        rows.append(row)
+        del kp, vp, q, o, ws, bt
+        torch.cuda.empty_cache()
+    return rows
+
+
 def headline(b, steps: int, warmup: int, counters):
     """The headline bench line: whole steps (append + attention) on workload b."""
     import torch
@@ -746,6 +790,8 @@ def main():
                     help="first copy MIB MiB device-to-device (a reference kernel for HBM counters)")
     ap.add_argument("--split-sweep", action="store_true",
                     help="only measure the split-KV crossover on long-context decode batches and exit")
+    ap.add_argument("--routing-sweep", action="store_true",
+                    help="only measure GQA decode rows on the matrix cores against the vector kernel and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path needs no collective); --gpus {args.gpus} is not run.",
@@ -758,6 +804,9 @@ def main():
     pk.load_library()
     if args.split_sweep:
         print(json.dumps({"split_sweep": split_sweep()}), flush=True)
+        return
+    if args.routing_sweep:
+        print(json.dumps({"routing_sweep": routing_sweep()}), flush=True)
         return
     counters = load_counters()
     if args.copy_calibration > 0:
