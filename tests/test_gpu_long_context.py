@@ -6,7 +6,10 @@ section 2 (one long context cut into partitions).  Zero-query signature values a
 the gate at every length (the margins are derived on the CPU in test_long_context_pins.py).
 Every case runs with both kernels (default routing, vector only) and three plans: never split
 (whole partitions of up to 1025 tiles, so the matrix-core kernel streams far past its first 128
-tiles), the adaptive split of pensieve_attn_fwd, and the explicit 32-way split pair.
+tiles), the adaptive split of pensieve_attn_fwd, and the explicit 32-way split pair.  The bf16
+cases also run on E4M3 pools ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3)) with both
+scales 1, where the structured values are exact codes (pinned on the CPU), so the same closed
+forms and gates apply.
 """
 
 import numpy as np
@@ -43,11 +46,16 @@ def _longest_matrix_partition_tiles(gb):
     return best
 
 
-@pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8), ("f16", 1)])
-def test_signature_zero_query_at_long_lengths(dtype, group):
+CASES = [pytest.param(dt, g, f8, id=f"{dt}-g{g}" + ("-e4m3" if f8 else ""))
+         for dt, g, f8 in [("bf16", 1, None), ("bf16", 8, None), ("f16", 1, None), ("bf16", 1, (1.0, 1.0)),
+                           ("bf16", 8, (1.0, 1.0))]]
+
+
+@pytest.mark.parametrize("dtype,group,kv_fp8", CASES)
+def test_signature_zero_query_at_long_lengths(dtype, group, kv_fp8):
     b = signature_batch(dtype, group)
-    _say(f"signature {dtype} G={group}: L={b.context_lens.tolist()} T={b.total_q}")
-    gb = upload(b)
+    _say(f"signature {dtype} G={group} fp8={kv_fp8}: L={b.context_lens.tolist()} T={b.total_q}")
+    gb = upload(b, kv_fp8=kv_fp8)
     assert _longest_matrix_partition_tiles(gb) > 128
     exp = signature_expected(b)
     tol = signature_tol(exp, dtype)
@@ -61,11 +69,11 @@ def test_signature_zero_query_at_long_lengths(dtype, group):
             assert not bad.any(), (kname, plan, np.argwhere(bad)[:5].tolist())
 
 
-@pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8), ("f16", 1)])
-def test_onehot_rows_in_every_tile(dtype, group):
+@pytest.mark.parametrize("dtype,group,kv_fp8", CASES)
+def test_onehot_rows_in_every_tile(dtype, group, kv_fp8):
     b = onehot_batch(dtype, group)
-    _say(f"one-hot {dtype} G={group}: L={b.context_lens.tolist()} rows per request {b.q_lens.tolist()}")
-    gb = upload(b)
+    _say(f"one-hot {dtype} G={group} fp8={kv_fp8}: L={b.context_lens.tolist()} rows per request {b.q_lens.tolist()}")
+    gb = upload(b, kv_fp8=kv_fp8)
     assert gb.q_pos is not None
     assert _longest_matrix_partition_tiles(gb) > 128
     exp = onehot_expected(b)

@@ -33,6 +33,18 @@ def test_signature_values_are_exact_in_storage(dtype):
     assert set(np.unique(v).tolist()) == {-A, 0.0, A}
 
 
+def test_structured_values_are_exact_in_e4m3_at_scale_one():
+    """The GPU runs the structured cases on E4M3 pools too, with both scales 1: every V value of the
+    signature pattern (0, +-A) and every K and V value of the one-hot pattern (+-1) is an E4M3 code,
+    so the pools hold the same values as the 16-bit pools and the closed forms and margins carry
+    over unchanged; the signature's random K may round, but its queries are zero."""
+    v = signature_v(4097, 2, 128, 3).astype(np.float64)
+    assert np.array_equal(oracle.e4m3_decode(oracle.e4m3_encode(v)), v)
+    pm = np.array([-1.0, 1.0])
+    assert np.array_equal(oracle.e4m3_decode(oracle.e4m3_encode(pm)), pm)
+    assert A <= oracle.E4M3_MAX
+
+
 @pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8), ("f16", 1)])
 def test_signature_expected_is_the_mean_and_every_slip_is_far(dtype, group):
     b = signature_batch(dtype, group)
