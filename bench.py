@@ -49,9 +49,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}   # dense MFMA (fp32: vector peak)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 MIN_CPU_S = 10.0               # cpu_baseline times at least this much oracle work (within its budget)
-KERNEL_SOURCES = {
-    "attn_mfma": ["attn_mfma.hip", "device_common.h"],
-    "attn_vector": ["attn_vector.hip", "device_common.h"],
+KERNEL_SOURCES = {    # what a counter profile depends on: the kernel and the planner that orders its items
+    "attn_mfma": ["attn_mfma.hip", "device_common.h", "api.cpp"],
+    "attn_vector": ["attn_vector.hip", "device_common.h", "api.cpp"],
     "kv_append": ["kv_append.hip", "device_common.h"],
     "split_merge": ["split_merge.hip", "device_common.h"],
 }
