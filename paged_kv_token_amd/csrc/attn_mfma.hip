@@ -383,13 +383,20 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // S^T of one tile for this lane's row: s[mb][v] is key t0 + 32 mb + 16 (v / 8) + 8 h2 + v % 8.
   // K operands are read in batches of four k-steps for both 32-key halves, and the two
   // independent accumulator chains alternate, so LDS latency overlaps the MFMAs.
-  auto qk = [&](const uint8_t* ks_base, f32x16* sc) {
+  constexpr int KPRE_STEPS = 3;              // k-steps of K operands read before the row max
+  auto qk = [&](const uint8_t* ks_base, f32x16* sc, const vec8 (*kfirst)[2]) {
     sc[0] = f32x16{};
     sc[1] = f32x16{};
 #pragma unroll
     for (int k0 = 0; k0 < KS; k0 += 4) {
       vec8 kop[4][2];
-      if constexpr (F8) {
+      if (kfirst && k0 == 0) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            kop[kk][mb] = kk < KPRE_STEPS ? kfirst[kk][mb] : operand(ks_base + krd[kk] + mb * 32 * KROW);
+      } else if constexpr (F8) {
 #pragma unroll
         for (int kk = 0; kk < 4; kk += 2)
 #pragma unroll
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
     lds_barrier();
-    if (!wave_idle) qk(lds, s_cur);
+    if (!wave_idle) qk(lds, s_cur, nullptr);
   }
 
   // One tile: PAR is ti & 1 (the K stage of tile ti + 1 and the V stage of tile ti are
@@ -464,6 +471,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       lds_barrier();
     }
     if (wave_idle) return;                    // loads and barriers only
+    // 2-byte pools at d = 128: the K operands of the first KPRE_STEPS k-steps of the next tile's
+    // QK are read here, before the row max below, so that their LDS latency overlaps it (the next
+    // tile's scores are not live yet, so their registers are free).
+    constexpr bool KPRE = !F8 && D == 128;
+    vec8 kfirst[4][2] = {};
+    if constexpr (KPRE) {
+#pragma unroll
+      for (int kk = 0; kk < KPRE_STEPS; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) kfirst[kk][mb] = operand(k_next + krd[kk] + mb * 32 * KROW);
+    }
     // Masking (diagonal and tail tiles only): key offset 32 mb + 16 (v / 8) + v % 8 from
     // t0 + 8 h2 is visible iff it is <= lim.
     if ((t0 + KT - 1 > pmin_w) || (t0 + KT > t_valid)) {
@@ -497,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     // this tile (VALU), then O^T += V^T P^T.  The next tile's QK is computed even when it
     // does not exist (its result is then never read), so that no branch splits the region
     // and the scheduler can interleave the MFMAs with the exponentials.
-    qk(k_next, s_nxt);
+    qk(k_next, s_nxt, KPRE ? kfirst : nullptr);
     const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
     vec8 pb[4];
 #pragma unroll
@@ -527,20 +545,22 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     // exponentials of this tile run while the QK MFMAs of the next one execute, and the weight
     // conversions and row sums while the PV MFMAs do.  Left to itself the scheduler issues the QK
     // MFMAs back to back, each behind its own LDS operand reads.  At D = 128 the LDS operand
-    // reads are also placed: six K reads (and twelve transposing V reads, six V^T operands) are
-    // issued before the first MFMA of their phase and one more (two) after each MFMA, so every
-    // MFMA finds its operand loaded several MFMAs earlier (253 VGPRs, no spills; 2-3 % on the
-    // long-context and GQA recompute batches; eight and sixteen ahead spill), and the QK phase
-    // takes two VALU instructions per MFMA (1 % on the long-context batch).  E4M3 tiles keep
-    // the scheduler's order: their operand widening adds four VALU conversions per MFMA, and the
-    // same pattern made them slower.
-    constexpr int KA = 6, VA = 12;           // K and V reads issued ahead of their MFMAs
+    // reads are also placed: six K reads were issued before the row max (their latency overlaps
+    // it; 1 % on the GQA recompute batch), two more go out before the first QK MFMA and the rest
+    // one after each MFMA; twelve transposing V reads (six V^T operands) go out before the first
+    // PV MFMA and two after each, so every MFMA finds its operand loaded several MFMAs earlier
+    // (253-256 VGPRs, no spills; 2-3 % on the long-context and GQA recompute batches; eight and
+    // sixteen reads ahead spill, and so do eight K reads before the row max at G = 8), and the
+    // QK phase takes two VALU instructions per MFMA (1 % on the long-context batch).  E4M3 tiles
+    // keep the scheduler's order: their operand widening adds four VALU conversions per MFMA,
+    // and the same pattern made them slower.
+    constexpr int VA = 12;                   // V reads issued ahead of the first PV MFMA
     if constexpr (!F8 && D == 128) {
-      __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);      // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS reads
 #pragma unroll
       for (int i = 0; i < 2 * KS; ++i) {                       // QK of the next tile
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-        if (i < 2 * KS - KA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < 2 * KS - 2 * KPRE_STEPS - 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);     // two VALU instructions
       }
       __builtin_amdgcn_sched_group_barrier(0x100, VA, 0);
