@@ -30,6 +30,10 @@ from workloads import custom_batch
 
 LONG_HIST = (32768, 40960, 49152, 65536)
 LONG_NEW = (1, 1, 512, 1)
+# The largest contexts the structured tests reach: a decode row on 262 144 keys (4 096 tiles of 64)
+# beside a 64-row prefill on 131 072 history tokens.
+MAX_HIST = (262143, 131072)
+MAX_NEW = (1, 64)
 A = 256.0
 
 
@@ -52,9 +56,11 @@ def signature_v(L: int, hkv: int, d: int, r: int) -> np.ndarray:
     return v
 
 
-def signature_batch(dtype: str, group: int, hkv: int = 2, d: int = 128, seed: int = 301):
-    """The long-context workload's lengths and rows, zero queries, signature V, random K."""
-    b = custom_batch(list(LONG_HIST), list(LONG_NEW), num_heads=hkv * group, num_kv_heads=hkv, head_dim=d,
+def signature_batch(dtype: str, group: int, hkv: int = 2, d: int = 128, seed: int = 301, hist=LONG_HIST,
+                    new=LONG_NEW):
+    """Zero queries, signature V, random K; the long-context workload's lengths and rows unless
+    hist / new give others."""
+    b = custom_batch(list(hist), list(new), num_heads=hkv * group, num_kv_heads=hkv, head_dim=d,
                      dtype=dtype, seed=seed, name=f"long_signature_{dtype}_g{group}")
     b.q_fn = lambda r: np.zeros((int(b.q_lens[r]), b.num_heads, d), np.float32)
     b.v_fn = lambda r: signature_v(int(b.context_lens[r]), hkv, d, r)

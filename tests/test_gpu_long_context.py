@@ -9,7 +9,9 @@ Every case runs with both kernels (default routing, vector only) and three plans
 tiles), the adaptive split of pensieve_attn_fwd, and the explicit 32-way split pair.  The bf16
 cases also run on E4M3 pools ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3)) with both
 scales 1, where the structured values are exact codes (pinned on the CPU), so the same closed
-forms and gates apply.
+forms and gates apply.  The largest context (a decode row on 262 144 keys, 4 096 tiles, beside a
+64-row prefill on 131 072 history tokens) runs the signature case through the same plans plus
+the 256-way split pair, the most partitions a request can have.
 """
 
 import numpy as np
@@ -17,7 +19,8 @@ import pytest
 
 import paged_kv_token_amd as pk
 from gpu_harness import run_attn, run_split, to_f64, upload
-from long_cases import ONEHOT_TOL, onehot_batch, onehot_expected, signature_batch, signature_expected, signature_tol
+from long_cases import (MAX_HIST, MAX_NEW, ONEHOT_TOL, onehot_batch, onehot_expected, signature_batch,
+                        signature_expected, signature_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,8 +33,8 @@ def _say(msg):
 
 
 def _run(gb, plan, kflag):
-    if plan == "split32":
-        return to_f64(run_split(gb, 32, kflag)[3])
+    if plan.startswith("split"):
+        return to_f64(run_split(gb, int(plan[5:]), kflag)[3])
     return to_f64(run_attn(gb, kflag | (pk.PENSIEVE_FLAG_NO_SPLIT if plan == "no_split" else 0)))
 
 
@@ -83,3 +86,20 @@ def test_onehot_rows_in_every_tile(dtype, group, kv_fp8):
             err = np.abs(got - exp)
             _say(f"  {kname}/{plan}: max abs err {float(err.max()):.3e}")
             assert np.all(np.isfinite(got)) and float(err.max()) <= ONEHOT_TOL, (kname, plan)
+
+
+@pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8)])
+def test_signature_zero_query_at_the_largest_context(dtype, group):
+    b = signature_batch(dtype, group, hist=MAX_HIST, new=MAX_NEW, seed=303)
+    _say(f"largest context {dtype} G={group}: L={b.context_lens.tolist()} T={b.total_q}")
+    gb = upload(b)
+    assert _longest_matrix_partition_tiles(gb) >= 2049
+    exp = signature_expected(b)
+    tol = signature_tol(exp, dtype)
+    for kname, kflag in KERNELS.items():
+        for plan in PLANS + ("split256",):
+            got = _run(gb, plan, kflag)
+            assert np.all(np.isfinite(got)), (kname, plan)
+            worst = float(np.max(np.abs(got - exp) / tol))
+            _say(f"  {kname}/{plan}: worst |err|/tol {worst:.3f}")
+            assert worst <= 1.0, (kname, plan, np.argwhere(np.abs(got - exp) > tol)[:5].tolist())

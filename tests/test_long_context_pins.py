@@ -18,8 +18,8 @@ import numpy as np
 import pytest
 
 import oracle
-from long_cases import (A, ONEHOT_TOL, onehot_batch, onehot_expected, signature_batch, signature_expected,
-                        signature_tol, signature_v)
+from long_cases import (A, MAX_HIST, MAX_NEW, ONEHOT_TOL, onehot_batch, onehot_expected, signature_batch,
+                        signature_expected, signature_tol, signature_v)
 from workloads.batches import _to_storage
 
 SLIPS = (-64, -16, -1, 1, 16, 64)
@@ -45,9 +45,11 @@ def test_structured_values_are_exact_in_e4m3_at_scale_one():
     assert A <= oracle.E4M3_MAX
 
 
-@pytest.mark.parametrize("dtype,group", [("bf16", 1), ("bf16", 8), ("f16", 1)])
-def test_signature_expected_is_the_mean_and_every_slip_is_far(dtype, group):
-    b = signature_batch(dtype, group)
+@pytest.mark.parametrize("dtype,group,lengths", [("bf16", 1, "long"), ("bf16", 8, "long"), ("f16", 1, "long"),
+                                                  ("bf16", 1, "max")])
+def test_signature_expected_is_the_mean_and_every_slip_is_far(dtype, group, lengths):
+    b = (signature_batch(dtype, group) if lengths == "long"
+         else signature_batch(dtype, group, hist=MAX_HIST, new=MAX_NEW, seed=303))
     exp = signature_expected(b)
     tol = signature_tol(exp, dtype)
     G = b.num_heads // b.num_kv_heads
