@@ -518,8 +518,16 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
     s.owned = false;
     size_t cap = 2 * Stager::kSlotBytes;
     while (cap < bytes) cap *= 2;
-    if ((e = hipHostMalloc(&s.host, cap, hipHostMallocMapped)) != hipSuccess) return e;
-    if ((e = hipHostGetDevicePointer(&s.mapped, s.host, 0)) != hipSuccess) return e;
+    if ((e = hipHostMalloc(&s.host, cap, hipHostMallocMapped)) != hipSuccess) {
+      s.host = nullptr;
+      return e;
+    }
+    if ((e = hipHostGetDevicePointer(&s.mapped, s.host, 0)) != hipSuccess) {
+      (void)hipHostFree(s.host);
+      s.host = nullptr;
+      s.mapped = nullptr;
+      return e;
+    }
     s.cap = cap;
     s.owned = true;
   }

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import paged_kv_token_amd as pk
-from gpu_harness import run_attn, to_host_storage, upload
+from gpu_harness import run_attn, to_f64, to_host_storage, upload
 from workloads import custom_batch
 
 pytestmark = pytest.mark.gpu
@@ -97,3 +97,27 @@ def test_graph_capture_is_refused():
     torch.cuda.synchronize()
     assert float(x[0]) == 1.0
     assert not torch.any(o != 0)
+
+
+def test_work_list_beyond_a_staging_slot():
+    """A work list larger than one staging slot (19 200 items, 600 KB against 512 KiB slots) goes
+    up through a page-locked buffer of its own; two calls in a row match the oracle, and a small
+    batch afterwards still does."""
+    from oracle_helpers import oracle_output
+    rng = np.random.default_rng(5)
+    R = 600
+    big = custom_batch(rng.integers(16, 300, size=R), np.ones(R, np.int64), num_heads=32, num_kv_heads=32,
+                       head_dim=64, dtype="f16", seed=91)
+    gb = upload(big)
+    n_items = len(pk.pensieve_debug_plan(gb.desc))
+    assert n_items * 32 > 512 * 1024
+    ref = oracle_output(big)
+    for call in range(2):
+        err = float(np.max(np.abs(to_f64(run_attn(gb)) - ref)))
+        _say(f"{n_items} items, call {call}: max abs err {err:.3e}")
+        assert err <= 1e-2
+    small = _mixed()
+    ref_s = oracle_output(small)
+    err = float(np.max(np.abs(to_f64(run_attn(upload(small))) - ref_s)))
+    _say(f"small batch after: max abs err {err:.3e}")
+    assert err <= 1e-2
