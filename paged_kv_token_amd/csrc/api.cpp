@@ -541,13 +541,14 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
 
 // The staging buffer may be reused once `stream` has passed this point, or, when the slot's event
 // is already attached to the launch that read the buffer (`recorded`), once that launch is done.
+// If the event cannot be recorded the slot stays held: nothing would tell when the copy is done.
 hipError_t stage_release(Stager::Slot* slot, hipStream_t stream, bool recorded = false) {
   hipError_t e;
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
   std::lock_guard<std::mutex> lk(st->mu);
-  slot->in_use = false;
   if (!recorded && (e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
+  slot->in_use = false;
   slot->pending = true;
   return hipSuccess;
 }
@@ -587,7 +588,7 @@ struct TraceEntry {
 std::mutex g_trace_mu;
 bool g_trace_on = false;
 int g_trace_every = 1;                // time every n-th launch of each kernel kind
-long long g_trace_seen[5] = {};  // indexed by TraceKernel       // launches per kernel kind since tracing was enabled
+long long g_trace_seen[5] = {};  // launches per kernel kind (TraceKernel) since tracing was enabled
 std::deque<TraceEntry> g_pending;
 std::vector<pensieve_trace_record> g_records;
 hipError_t g_trace_error = hipSuccess;
@@ -636,7 +637,11 @@ struct TraceScope {
     harvest_finished();
     if (g_records.size() + g_pending.size() >= kMaxTraceEntries) return;
     entry = {kernel, items, trace_event(), trace_event()};
-    if (!entry.start || !entry.stop) return;
+    if (!entry.start || !entry.stop) {   // keep whichever event was made for a later launch
+      if (entry.start) g_event_pool.push_back(entry.start);
+      if (entry.stop) g_event_pool.push_back(entry.stop);
+      return;
+    }
     pk::launch_events() = {entry.start, entry.stop};
     active = true;
   }
@@ -665,10 +670,18 @@ hipError_t concurrency_for_current_device(Concurrency** out) {
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lk(g_conc_mu);
   Concurrency& c = g_conc[dev];
-  if (!c.side) {
-    if ((e = hipStreamCreateWithFlags(&c.side, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&c.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&c.join, hipEventDisableTiming)) != hipSuccess) return e;
+  if (!c.side) {   // all three or none: a partial set is destroyed and the next call tries again
+    Concurrency n;
+    if ((e = hipStreamCreateWithFlags(&n.side, hipStreamNonBlocking)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) == hipSuccess &&
+        (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) == hipSuccess) {
+      c = n;
+    } else {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.side) (void)hipStreamDestroy(n.side);
+      return e;
+    }
   }
   *out = &c;
   return hipSuccess;
