@@ -8,7 +8,11 @@
 //
 // One wave per (row, head): lanes read the P (m, l) pairs, reduce the max and
 // the weight sum across the wave, park the weights in LDS, then stream the P
-// partial rows of D fp32 values with coalesced loads (lane = dim).
+// partial rows of D fp32 values with 16-byte loads: D / 4 lanes cover one
+// partition row (four dims each), so one pass reads 64 / (D / 4) partitions
+// (two at D = 128, four at D = 64), and the lanes holding the same dims add
+// their sums at the end (each partition's term is still one fma into one
+// running sum per lane; the lanes' sums are added in a fixed order).
 //
 // Partials are laid out [row][head][P_stride]; with a row map, partial row c
 // holds output row rowmap[2c] and only its first rowmap[2c + 1] partitions
@@ -60,15 +64,25 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float* __restric
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const float inv = (W > 0.f) ? 1.f / W : 0.f;
+  constexpr int LPR = D / 4;                // lanes per partition row
+  constexpr int PPP = 64 / LPR;             // partitions per pass
+  const int q4 = lane % LPR;                // dims 4 q4 .. 4 q4 + 3
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p = lane / LPR; p < P; p += PPP) {
+    const float wgt = s_w[wv][p];
+    if (wgt != 0.f) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (base + p) * D + 4 * q4);
 #pragma unroll
-  for (int d0 = 0; d0 < D; d0 += 64) {
-    const int d = d0 + lane;
-    float acc = 0.f;
-    for (int p = 0; p < P; ++p) {
-      const float wgt = s_w[wv][p];
-      if (wgt != 0.f) acc = fmaf(wgt, part_o[(base + p) * D + d], acc);
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, v[e], acc[e]);
     }
-    store_elem<DT>(o, out * D + d, acc * inv);
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_elem<DT>(o, out * D + 4 * q4 + e, acc[e] * inv);
   }
 }
 
