@@ -298,14 +298,15 @@ def test_no_split_flag_keeps_every_request_whole(lib):
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_covers_random_batches(lib, seed):
     """Random ragged batches (empty requests, first turns, long contexts, every head grouping,
-    both kernels, adaptive and fixed splits): every (row, head, partition) is planned once."""
+    both kernels, head groups that do and do not divide 32, adaptive and fixed splits): every (row,
+    head, partition) is planned once."""
     rng = np.random.default_rng(500 + seed)
     R = int(rng.integers(1, 24))
     hist = rng.integers(0, 20000 if seed % 3 == 0 else 2000, size=R)
     new = np.where(rng.random(R) < 0.2, 0, rng.integers(1, 300, size=R))
     hist = np.where((new == 0) & (hist == 0), 1, hist)
     hkv = int(rng.choice([1, 2, 4]))
-    G = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12]))
     b = custom_batch(hist, new, num_heads=hkv * G, num_kv_heads=hkv, head_dim=int(rng.choice([64, 128])),
                      dtype=str(rng.choice(["f16", "bf16", "f32"])), seed=seed)
     for flags in (0, pk.PENSIEVE_FLAG_VECTOR_ONLY, pk.PENSIEVE_FLAG_NO_SPLIT):

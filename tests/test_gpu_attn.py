@@ -48,6 +48,18 @@ CASES = {
                                              num_kv_heads=2, head_dim=128, dtype="bf16", seed=25),
     "f32_d128_gqa2": lambda: custom_batch([30, 0, 77], [3, 40, 1], num_heads=4, num_kv_heads=2, head_dim=128,
                                           dtype="f32", seed=24),
+    # Head groups that do not divide 32 run on the vector kernel in items of up to 8 query vectors
+    # that hold whole tokens' groups where they fit (G = 3, 5, 6) or part of one group (G = 12, 64).
+    "gqa5_f16": lambda: custom_batch([300, 0, 2000, 77], [5, 40, 1, 130], num_heads=10, num_kv_heads=2,
+                                     head_dim=128, dtype="f16", seed=27),
+    "gqa3_d64_bf16": lambda: custom_batch([40, 900, 16], [33, 1, 17], num_heads=12, num_kv_heads=4, head_dim=64,
+                                          dtype="bf16", seed=28),
+    "gqa6_f32": lambda: custom_batch([100, 5], [7, 60], num_heads=12, num_kv_heads=2, head_dim=64, dtype="f32",
+                                     seed=29),
+    "gqa12_bf16": lambda: custom_batch([600, 31], [2, 45], num_heads=24, num_kv_heads=2, head_dim=128,
+                                       dtype="bf16", seed=30),
+    "gqa64_f16": lambda: custom_batch([1500, 64], [1, 9], num_heads=64, num_kv_heads=1, head_dim=128, dtype="f16",
+                                      seed=32),
 }
 
 
