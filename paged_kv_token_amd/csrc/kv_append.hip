@@ -39,9 +39,14 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const u32x4* __restrict_
   const uint32_t c = i % CPR;
   const uint32_t row = i / CPR;               // token * Hkv + head
   const uint32_t t = row / (uint32_t)num_kv_heads, g = row % (uint32_t)num_kv_heads;
+  // The new row is read before the slot is tested: chunk i is in bounds whatever the slot holds,
+  // and both loads are then in flight together instead of one after the other.  The empty asm
+  // statement (no instruction) takes the row as an operand before the test, so the compiler
+  // cannot sink its load below it.
+  u32x4 x = __builtin_nontemporal_load((isv ? v_new : k_new) + i);
   const int s = slots[t];
+  asm volatile("" : "+v"(x));
   if (s < 0) return;
-  const u32x4 x = __builtin_nontemporal_load((isv ? v_new : k_new) + i);
   const size_t dst = (((size_t)(s >> 4) * num_kv_heads + g) * 16 + (size_t)(s & 15)) * ROW + (size_t)c * 16;
   __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>((isv ? v_pool : k_pool) + dst));
 }
@@ -89,14 +94,20 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(const uint8_t* __res
   const uint32_t c = i % CPR;
   const uint32_t row = i / CPR;
   const uint32_t t = row / (uint32_t)num_kv_heads, g = row % (uint32_t)num_kv_heads;
-  const int s = slots[t];
-  if (s < 0) return;
+  // As in the 16-bit append: the rows' loads are issued before the slot is tested.
   const size_t src = (size_t)i * 32;
+  u32x4 raw[4] = {__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_new + src)),
+                  __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_new + src + 16)),
+                  __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_new + src)),
+                  __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_new + src + 16))};
+  const int s = slots[t];
+  asm volatile("" : "+v"(raw[0]), "+v"(raw[1]), "+v"(raw[2]), "+v"(raw[3]));
+  if (s < 0) return;
   float kf[16], vf[16];
-  unpack16<SDT>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_new + src)), kf);
-  unpack16<SDT>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_new + src + 16)), kf + 8);
-  unpack16<SDT>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_new + src)), vf);
-  unpack16<SDT>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_new + src + 16)), vf + 8);
+  unpack16<SDT>(raw[0], kf);
+  unpack16<SDT>(raw[1], kf + 8);
+  unpack16<SDT>(raw[2], vf);
+  unpack16<SDT>(raw[3], vf + 8);
   u32x4 kc, vc;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
