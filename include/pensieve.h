@@ -53,9 +53,11 @@
  *   the calls' paths (callers pass workspace), but keeps three kinds of
  *   process-wide state, created on first use per device and held until the
  *   process ends: (1) a ring of 32 page-locked, device-mapped host slots
- *   (one 16 MiB slab, a slot grown alone past 512 KiB) through which
- *   pensieve_attn_fwd, pensieve_attn_split_partial and the swaps upload
- *   their host-built work lists with a small copy kernel on `stream`;
+ *   (one 16 MiB slab, a slot grown alone past 512 KiB, and an 8 KiB
+ *   page-locked flag array through which the copy kernel reports that it
+ *   has read a slot) through which pensieve_attn_fwd,
+ *   pensieve_attn_split_partial and the swaps upload their host-built work
+ *   lists with a small copy kernel on `stream`;
  *   (2) a non-blocking side stream with two events: when a plan mixes
  *   matrix-core and vector items and the matrix-core items alone cannot
  *   fill the GPU, the vector items run on it, forked from and joined back

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -19,6 +20,7 @@
 #include <deque>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <unordered_map>
 #include <vector>
 
@@ -451,11 +453,20 @@ struct Stager {
     hipEvent_t ev = nullptr;
     bool pending = false;
     bool in_use = false;      // handed out by stage_acquire, not yet given back by stage_release
+    // The slot's last use is over once every one of the flag_blocks workgroups of the copy
+    // kernel that read it has stored `seq` into its flag; with no such kernel (flag_blocks == 0)
+    // once `ev` has completed.
+    uint32_t seq = 0;
+    int flag_blocks = 0;
+    uint32_t* flags_host = nullptr;   // kStageCopyBlocks words of the flag array
+    uint32_t* flags_dev = nullptr;    // the same words as seen from the device
   };
   std::mutex mu;
   Slot slots[kSlots];
   int next = 0;
   void* slab = nullptr;
+  uint32_t* flags = nullptr;          // kSlots x kStageCopyBlocks words, page-locked and coherent
+  uint32_t seq = 0;                   // last sequence number handed out (0 is never used)
 };
 
 std::mutex g_stagers_mu;
@@ -473,6 +484,31 @@ Stager* stager_for_current_device(hipError_t* err) {
   return s;
 }
 
+// Wait until every workgroup of the copy kernel that last read slot `s` has stored the slot's
+// sequence number (no event on the stream: an event recorded between two kernels holds the next
+// one back by about 5 us).  Bounded: if the flags have not all arrived within two seconds, the
+// device is synchronised once, after which every launch enqueued before has finished; flags still
+// missing then are an error, not a hang.
+hipError_t wait_stage_flags(const Stager::Slot& s) {
+  auto arrived = [&s] {
+    for (int b = 0; b < s.flag_blocks; ++b)
+      if (__atomic_load_n(s.flags_host + b, __ATOMIC_ACQUIRE) != s.seq) return false;
+    return true;
+  };
+  const auto t0 = std::chrono::steady_clock::now();
+  for (unsigned spin = 1; !arrived(); ++spin) {
+    if (spin % 1024 == 0) {
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(2)) {
+        const hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return e;
+        return arrived() ? hipSuccess : hipErrorUnknown;
+      }
+      std::this_thread::yield();
+    }
+  }
+  return hipSuccess;
+}
+
 // Copy `bytes` from `src` into the next staging buffer of this device (waiting until the
 // buffer's previous use on the GPU has finished) and return its device mapping; the caller
 // enqueues the work that reads it, then calls stage_release on the same stream.
@@ -484,17 +520,27 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   if (!st->slab) {
     void* slab = nullptr;
     void* slab_mapped = nullptr;
+    void* flags = nullptr;
+    void* flags_mapped = nullptr;
+    constexpr size_t kFlagBytes = Stager::kSlots * pk::kStageCopyBlocks * sizeof(uint32_t);
     if ((e = hipHostMalloc(&slab, Stager::kSlots * Stager::kSlotBytes, hipHostMallocMapped)) != hipSuccess)
       return e;
-    if ((e = hipHostGetDevicePointer(&slab_mapped, slab, 0)) != hipSuccess) {
+    if ((e = hipHostGetDevicePointer(&slab_mapped, slab, 0)) != hipSuccess ||
+        (e = hipHostMalloc(&flags, kFlagBytes, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess ||
+        (e = hipHostGetDevicePointer(&flags_mapped, flags, 0)) != hipSuccess) {
+      if (flags) (void)hipHostFree(flags);
       (void)hipHostFree(slab);
       return e;
     }
+    std::memset(flags, 0, kFlagBytes);
     st->slab = slab;
+    st->flags = static_cast<uint32_t*>(flags);
     for (int i = 0; i < Stager::kSlots; ++i) {
       st->slots[i].host = static_cast<uint8_t*>(st->slab) + i * Stager::kSlotBytes;
       st->slots[i].mapped = static_cast<uint8_t*>(slab_mapped) + i * Stager::kSlotBytes;
       st->slots[i].cap = Stager::kSlotBytes;
+      st->slots[i].flags_host = st->flags + i * pk::kStageCopyBlocks;
+      st->slots[i].flags_dev = static_cast<uint32_t*>(flags_mapped) + i * pk::kStageCopyBlocks;
     }
   }
   // The next slot that no other call holds between its acquire and its release.
@@ -507,7 +553,7 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   Stager::Slot& s = st->slots[pick];
   st->next = (pick + 1) % Stager::kSlots;
   if (s.pending) {
-    if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return e;
+    if ((e = s.flag_blocks > 0 ? wait_stage_flags(s) : hipEventSynchronize(s.ev)) != hipSuccess) return e;
     s.pending = false;
   }
   if (s.cap < bytes) {
@@ -533,21 +579,26 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   }
   if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
   std::memcpy(s.host, src, bytes);
+  if (++st->seq == 0) st->seq = 1;
+  s.seq = st->seq;
+  s.flag_blocks = 0;
   s.in_use = true;
   *mapped = s.mapped;
   *slot_out = &s;
   return hipSuccess;
 }
 
-// The staging buffer may be reused once `stream` has passed this point, or, when the slot's event
-// is already attached to the launch that read the buffer (`recorded`), once that launch is done.
-// If the event cannot be recorded the slot stays held: nothing would tell when the copy is done.
-hipError_t stage_release(Stager::Slot* slot, hipStream_t stream, bool recorded = false) {
+// The staging buffer may be reused once `stream` has passed this point, or, when `flag_blocks`
+// workgroups of a copy kernel read it and store the slot's sequence number when done, once they
+// all have.  If the event cannot be recorded the slot stays held: nothing would tell when the
+// work that reads the buffer is done.
+hipError_t stage_release(Stager::Slot* slot, hipStream_t stream, int flag_blocks = 0) {
   hipError_t e;
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
   std::lock_guard<std::mutex> lk(st->mu);
-  if (!recorded && (e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
+  if (flag_blocks == 0 && (e = hipEventRecord(slot->ev, stream)) != hipSuccess) return e;
+  slot->flag_blocks = flag_blocks;
   slot->in_use = false;
   slot->pending = true;
   return hipSuccess;
@@ -702,17 +753,17 @@ int device_cu_count() {
 }
 
 // A work list in a staging buffer, given back after the call's last launch on every return path.
-// Its reuse waits for the slot's event: recorded by the copy kernel's own completion when the
-// copy was launched (`attached`), else on the caller's stream at the release.
+// Its reuse waits for the copy kernel's flags when the copy was launched (`flag_blocks`
+// workgroups), else for an event recorded on the caller's stream at the release.
 struct StagedList {
   Stager::Slot* slot = nullptr;
   hipStream_t stream = nullptr;
-  bool attached = false;
+  int flag_blocks = 0;
   hipError_t release() {
     if (!slot) return hipSuccess;
     Stager::Slot* s = slot;
     slot = nullptr;
-    return stage_release(s, stream, attached);
+    return stage_release(s, stream, flag_blocks);
   }
   ~StagedList() { (void)release(); }
 };
@@ -730,11 +781,9 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     void* mapped = nullptr;
     hipError_t e = stage_acquire(src, bytes, &mapped, &staged.slot);
     if (e != hipSuccess) return e;
-    if (bytes % 16 == 0) {
-      e = pk::launch_stage_copy(mapped, ws, bytes, stream, staged.slot->ev);
-      staged.attached = e == hipSuccess;
-      return e;
-    }
+    if (bytes % 16 == 0)
+      return pk::launch_stage_copy(mapped, ws, bytes, stream, staged.slot->flags_dev, staged.slot->seq,
+                                   &staged.flag_blocks);
     return hipMemcpyAsync(ws, staged.slot->host, bytes, hipMemcpyHostToDevice, stream);
   };
   hipError_t e;

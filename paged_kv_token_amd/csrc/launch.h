@@ -53,9 +53,13 @@ hipError_t launch_kv_swap(const void* src_k, const void* src_v, void* dst_k, voi
                           int n, int64_t block_bytes, hipStream_t stream);
 
 // Copy `bytes` (a multiple of 16) from a device-mapped page-locked host buffer to device
-// memory with a kernel on `stream`; `done` (nullable) is recorded by the copy's completion.
+// memory with a kernel of at most kStageCopyBlocks workgroups on `stream`.  With `done` (a
+// device-mapped page-locked array of kStageCopyBlocks words) each workgroup stores `seq` into
+// done[its index] once its reads of the source are complete; *blocks_out (nullable) receives the
+// number of workgroups launched.
+constexpr int kStageCopyBlocks = 64;
 hipError_t launch_stage_copy(const void* src_mapped, void* dst, size_t bytes, hipStream_t stream,
-                             hipEvent_t done = nullptr);
+                             uint32_t* done = nullptr, uint32_t seq = 0, int* blocks_out = nullptr);
 
 // Size of the library-owned device scratch of pensieve_attn_fwd_noalloc (one array per GPU).
 constexpr size_t kScratchBytes = (size_t)64 << 20;
