@@ -121,3 +121,44 @@ def test_work_list_beyond_a_staging_slot():
     err = float(np.max(np.abs(to_f64(run_attn(upload(small))) - ref_s)))
     _say(f"small batch after: max abs err {err:.3e}")
     assert err <= 1e-2
+
+
+def test_staging_ring_reuse_while_the_host_runs_ahead():
+    """120 attention calls enqueued back to back on one stream with no host wait, over three
+    batches with different work lists, so the host laps the 32-slot staging ring while copies of
+    earlier calls may still be pending (a slot is refilled only after the copy kernel that read it
+    has reported, through its flags, that it is done); a swap-out after every seventh call takes
+    the other way of recycling a slot (an event).  Every output equals bitwise that of a
+    synchronised call of its batch."""
+    import torch
+    rng = np.random.default_rng(11)
+    batches = [
+        _mixed(),
+        custom_batch([3000] * 8, [64] * 8, num_heads=32, num_kv_heads=32, head_dim=128, dtype="bf16", seed=62),
+        custom_batch(rng.integers(100, 3000, size=64), np.ones(64, np.int64), num_heads=16, num_kv_heads=4,
+                     head_dim=64, dtype="f16", seed=63),
+    ]
+    gbs = [upload(b) for b in batches]
+    refs = [to_host_storage(run_attn(gb), gb.batch.dtype) for gb in gbs]
+    wss = [torch.empty(max(pk.pensieve_attn_workspace_size(gb.desc), 256), dtype=torch.uint8, device="cuda")
+           for gb in gbs]
+    g0 = gbs[0]
+    blocks = g0.batch.block_tables[0, :4].tolist()
+    k_host = torch.empty((4,) + tuple(g0.k_pool.shape[1:]), dtype=g0.k_pool.dtype).pin_memory()
+    v_host = torch.empty((4,) + tuple(g0.v_pool.shape[1:]), dtype=g0.v_pool.dtype).pin_memory()
+    outs = []
+    for i in range(120):
+        j = i % 3
+        gb = gbs[j]
+        o = torch.empty_like(gb.q)
+        pk.pensieve_attn_fwd(gb.desc, gb.q, gb.k_pool, gb.v_pool, gb.block_tables, gb.context_lens, gb.cu_q_lens,
+                             gb.q_pos, o, wss[j])
+        outs.append((j, o))
+        if i % 7 == 6:
+            pk.pensieve_kv_swap_out(g0.k_pool, g0.v_pool, k_host, v_host, blocks, list(range(4)))
+    torch.cuda.synchronize()
+    bad = [i for i, (j, o) in enumerate(outs) if not np.array_equal(to_host_storage(o, gbs[j].batch.dtype), refs[j])]
+    _say(f"120 calls enqueued without a wait: {len(bad)} outputs differ")
+    assert not bad
+    assert np.array_equal(k_host.cpu().numpy().view(np.uint16),
+                          g0.k_pool[torch.tensor(blocks, device="cuda")].cpu().numpy().view(np.uint16))
