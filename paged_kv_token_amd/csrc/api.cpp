@@ -516,7 +516,7 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
   hipError_t e;
   Stager* st = stager_for_current_device(&e);
   if (!st) return e;
-  std::lock_guard<std::mutex> lk(st->mu);
+  std::unique_lock<std::mutex> lk(st->mu);
   if (!st->slab) {
     void* slab = nullptr;
     void* slab_mapped = nullptr;
@@ -543,21 +543,38 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
       st->slots[i].flags_dev = static_cast<uint32_t*>(flags_mapped) + i * pk::kStageCopyBlocks;
     }
   }
-  // The next slot that no other call holds between its acquire and its release.
+  // The next slot that no other call holds between its acquire and its release.  When calls on
+  // other threads hold every slot, this one retries (without the lock) for up to ten seconds.
   int pick = -1;
-  for (int k = 0; k < Stager::kSlots && pick < 0; ++k) {
-    const int i = (st->next + k) % Stager::kSlots;
-    if (!st->slots[i].in_use) pick = i;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    for (int k = 0; k < Stager::kSlots && pick < 0; ++k) {
+      const int i = (st->next + k) % Stager::kSlots;
+      if (!st->slots[i].in_use) pick = i;
+    }
+    if (pick >= 0) break;
+    if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(10)) return hipErrorNotReady;
+    lk.unlock();
+    std::this_thread::yield();
+    lk.lock();
   }
-  if (pick < 0) return hipErrorNotReady;   // every slot is held by a call still enqueueing its work
   Stager::Slot& s = st->slots[pick];
   st->next = (pick + 1) % Stager::kSlots;
+  s.in_use = true;   // reserved: no other call takes it while this one waits; every failure below frees it
+  auto give_back = [&s](hipError_t err) {
+    s.in_use = false;
+    return err;
+  };
   if (s.pending) {
-    if ((e = s.flag_blocks > 0 ? wait_stage_flags(s) : hipEventSynchronize(s.ev)) != hipSuccess) return e;
+    // The wait runs without the lock, so that calls on other threads can take other slots meanwhile.
+    lk.unlock();
+    e = s.flag_blocks > 0 ? wait_stage_flags(s) : hipEventSynchronize(s.ev);
+    lk.lock();
+    if (e != hipSuccess) return give_back(e);
     s.pending = false;
   }
   if (s.cap < bytes) {
-    if (s.owned && (e = hipHostFree(s.host)) != hipSuccess) return e;
+    if (s.owned && (e = hipHostFree(s.host)) != hipSuccess) return give_back(e);
     s.host = nullptr;
     s.mapped = nullptr;
     s.cap = 0;            // stays empty if the allocation below fails
@@ -566,23 +583,22 @@ hipError_t stage_acquire(const void* src, size_t bytes, void** mapped, Stager::S
     while (cap < bytes) cap *= 2;
     if ((e = hipHostMalloc(&s.host, cap, hipHostMallocMapped)) != hipSuccess) {
       s.host = nullptr;
-      return e;
+      return give_back(e);
     }
     if ((e = hipHostGetDevicePointer(&s.mapped, s.host, 0)) != hipSuccess) {
       (void)hipHostFree(s.host);
       s.host = nullptr;
       s.mapped = nullptr;
-      return e;
+      return give_back(e);
     }
     s.cap = cap;
     s.owned = true;
   }
-  if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return e;
+  if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess) return give_back(e);
   std::memcpy(s.host, src, bytes);
   if (++st->seq == 0) st->seq = 1;
   s.seq = st->seq;
   s.flag_blocks = 0;
-  s.in_use = true;
   *mapped = s.mapped;
   *slot_out = &s;
   return hipSuccess;
