@@ -438,7 +438,9 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
 // Each device gets a small ring of page-locked, device-mapped host buffers; a
 // work list is copied into the next one and pulled into the workspace by a
 // small copy kernel on the caller's stream (one queue, no copy-engine handoff).
-// An event per buffer guards its reuse until the copy has finished.
+// A buffer is refilled only after the work that read it has finished: the copy
+// kernel's per-workgroup flags say so for work lists, an event for swap block
+// lists (read by the swap kernel itself).
 struct Stager {
   static constexpr int kSlots = 32;   // deep enough that a long swap does not hold up later calls
   // Every slot starts as a slice of one page-locked slab, so that the first pass over the ring
