@@ -81,6 +81,10 @@
  *   `stream`) and return INVALID_ARG on a violation before anything of the
  *   call is enqueued; they never read the pools to do so.  Debugging and
  *   tests only: it synchronises every call.
+ *   A call that finds its staging slot ((1) above) still being read by an
+ *   earlier copy waits for it up to PENSIEVE_STAGE_WAIT_US microseconds
+ *   (default 2 000 000, read at each such wait), then synchronises the
+ *   device once; a slot still unreported after that is an ERR_HIP failure.
  */
 #ifndef PENSIEVE_H
 #define PENSIEVE_H

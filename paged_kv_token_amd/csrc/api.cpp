@@ -488,19 +488,23 @@ Stager* stager_for_current_device(hipError_t* err) {
 
 // Wait until every workgroup of the copy kernel that last read slot `s` has stored the slot's
 // sequence number (no event on the stream: an event recorded between two kernels holds the next
-// one back by about 5 us).  Bounded: if the flags have not all arrived within two seconds, the
-// device is synchronised once, after which every launch enqueued before has finished; flags still
-// missing then are an error, not a hang.
+// one back by about 5 us).  Bounded: if the flags have not all arrived within two seconds
+// (PENSIEVE_STAGE_WAIT_US microseconds when set, read at each wait), the device is synchronised
+// once, after which every launch enqueued before has finished; flags still missing then are an
+// error, not a hang.
 hipError_t wait_stage_flags(const Stager::Slot& s) {
   auto arrived = [&s] {
     for (int b = 0; b < s.flag_blocks; ++b)
       if (__atomic_load_n(s.flags_host + b, __ATOMIC_ACQUIRE) != s.seq) return false;
     return true;
   };
+  if (arrived()) return hipSuccess;
+  long long limit_us = 2000000;
+  if (const char* v = std::getenv("PENSIEVE_STAGE_WAIT_US"); v && *v) limit_us = std::max(0LL, std::atoll(v));
   const auto t0 = std::chrono::steady_clock::now();
-  for (unsigned spin = 1; !arrived(); ++spin) {
+  for (unsigned spin = 0; !arrived(); ++spin) {
     if (spin % 1024 == 0) {
-      if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(2)) {
+      if (std::chrono::steady_clock::now() - t0 >= std::chrono::microseconds(limit_us)) {
         const hipError_t e = hipDeviceSynchronize();
         if (e != hipSuccess) return e;
         return arrived() ? hipSuccess : hipErrorUnknown;

@@ -123,14 +123,18 @@ def test_work_list_beyond_a_staging_slot():
     assert err <= 1e-2
 
 
-def test_staging_ring_reuse_while_the_host_runs_ahead():
+@pytest.mark.parametrize("wait_us", [None, "0"])
+def test_staging_ring_reuse_while_the_host_runs_ahead(wait_us, monkeypatch):
     """120 attention calls enqueued back to back on one stream with no host wait, over three
     batches with different work lists, so the host laps the 32-slot staging ring while copies of
     earlier calls may still be pending (a slot is refilled only after the copy kernel that read it
     has reported, through its flags, that it is done); a swap-out after every seventh call takes
     the other way of recycling a slot (an event).  Every output equals bitwise that of a
-    synchronised call of its batch."""
+    synchronised call of its batch.  With the wait limit at zero microseconds, a slot whose flags
+    have not arrived is recovered at once through the bounded wait's device synchronisation."""
     import torch
+    if wait_us is not None:
+        monkeypatch.setenv("PENSIEVE_STAGE_WAIT_US", wait_us)
     rng = np.random.default_rng(11)
     batches = [
         _mixed(),
@@ -158,7 +162,7 @@ def test_staging_ring_reuse_while_the_host_runs_ahead():
             pk.pensieve_kv_swap_out(g0.k_pool, g0.v_pool, k_host, v_host, blocks, list(range(4)))
     torch.cuda.synchronize()
     bad = [i for i, (j, o) in enumerate(outs) if not np.array_equal(to_host_storage(o, gbs[j].batch.dtype), refs[j])]
-    _say(f"120 calls enqueued without a wait: {len(bad)} outputs differ")
+    _say(f"120 calls enqueued without a wait (wait limit {wait_us} us): {len(bad)} outputs differ")
     assert not bad
     assert np.array_equal(k_host.cpu().numpy().view(np.uint16),
                           g0.k_pool[torch.tensor(blocks, device="cuda")].cpu().numpy().view(np.uint16))
