@@ -396,7 +396,11 @@ pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part
  *   {kernel, request, kv_head, first row in request, rows, partition,
  *    partitions, estimated cost, first query head of the group, heads}
  * with kernel 0 = vector path, 1 = matrix-core path, in launch order, and
- * sets *num_items to the full count.  No GPU is touched.
+ * sets *num_items to the full count.  No GPU is touched.  A matrix-core
+ * item holds up to 128 query vectors (rows x heads), or up to 256 in calls
+ * whose four-wave items would not fill one round of the GPU (about 512
+ * items) and that hold a request of more than 128 query vectors per KV
+ * head, with 2-byte pools: those run in eight-wave workgroups.
  */
 pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num_partitions,
                                     int32_t* items_host, int32_t max_items, int32_t* num_items);

@@ -65,7 +65,17 @@ constexpr int kVectorRowsMax = 8;    // query vectors per vector-kernel item
 // and 5.9 TB/s for G = 4, where the vector kernel, holding G query vectors per lane group,
 // reaches 2.7 and 5.5 TB/s.
 constexpr int kMatrixMinGroup = 4;
-constexpr int kMfmaRows = 128;       // query vectors per matrix-core item
+constexpr int kMfmaRows = 128;       // query vectors per matrix-core item (four waves)
+// Eight-wave matrix-core items (256 query vectors, one workgroup per CU) replace the four-wave
+// ones in calls whose four-wave items would not fill one round of workgroup slots
+// (kSplitTargetItems) and hold a request of more than kMfmaRows query vectors per KV head: each
+// busy CU then runs two waves per SIMD that share every K/V tile they load, and whole CUs are left
+// to the vector items beside them.  Long-context batch (a 512-row prefill beside three decode
+// requests): 0.825 -> 0.798 ms.  A call that fills the GPU keeps four-wave items, whose two
+// workgroups per CU overlap each other's barriers and load waits (the GQA recompute batch was
+// 0.60 -> 0.66 ms with eight-wave items).
+constexpr int kWideRows = 256;
+constexpr int kWideFlag = 1 << 8;    // Segment / PlannedItem param bit: eight-wave matrix-core items
 constexpr int kMaxPartitions = 256;
 // Adaptive split-KV of pensieve_attn_fwd: the plan aims at about kSplitTargetItems work
 // items of similar length -- one round of the matrix-core kernel, two workgroups on each of
@@ -142,7 +152,8 @@ enum Kernel { kVector = 0, kMatrix = 1 };
 struct PlannedItem {
   pk::WorkItem w;
   int kernel;
-  int param;        // vector: query vectors per item (1,2,4,8); matrix: group size
+  int param;        // vector: query vectors per item (1,2,4,8); matrix: group size, | kWideFlag
+                    // for eight-wave items
   long long cost;
 };
 
@@ -367,6 +378,19 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
     if (d->cu_q_lens_host[r + 1] > d->cu_q_lens_host[r]) reqs.push_back(r);
   std::stable_sort(reqs.begin(), reqs.end(),
                    [&](int a, int b) { return d->context_lens_host[a] > d->context_lens_host[b]; });
+  bool wide = false;
+  if (mat && d->kv_dtype != PENSIEVE_FP8_E4M3) {
+    long long narrow_items = 0;
+    bool long_rows = false;
+    for (int r : reqs) {
+      const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
+      if (!routes_to_matrix(mat, q, G)) continue;
+      narrow_items += items_per_kv_head(q, G, true) * d->num_kv_heads * parts[r];
+      long_rows = long_rows || (long long)q * G > kMfmaRows;
+    }
+    wide = long_rows && narrow_items < kSplitTargetItems;
+  }
+  const int mat_rows = wide ? kWideRows : kMfmaRows;
   for (int r : reqs) {
     const int L = d->context_lens_host[r];
     const int q = d->cu_q_lens_host[r + 1] - d->cu_q_lens_host[r];
@@ -378,14 +402,14 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
       const long long blocks = std::max(0LL, std::min(per, nblk - part * per));
       for (int g = 0; g < d->num_kv_heads; ++g) {
         if (use_matrix) {
-          const int tok_tile = kMfmaRows / G;
+          const int tok_tile = mat_rows / G;
           groups.push_back({0, (int)mat_items.size(), 0});
           for (int q0 = 0; q0 < q; q0 += tok_tile) {
             PlannedItem p{};
             const int qc = std::min(tok_tile, q - q0);
             p.w = {r, q0, qc, g, 0, G, part, P};
             p.kernel = kMatrix;
-            p.param = G;
+            p.param = G | (wide ? kWideFlag : 0);
             // An item streams the keys of its partition that its last (largest) position can
             // see, plus a fixed cost of about one block.
             const long long last = d->q_pos_host ? (long long)d->q_pos_host[d->cu_q_lens_host[r] + q0 + qc - 1]
@@ -830,11 +854,11 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
   bool has_matrix = false, has_vector = false;
   for (const Segment& s : plan.segments) (s.kernel == kMatrix ? has_matrix : has_vector) = true;
   Concurrency* conc = nullptr;
-  // Overlap only when the matrix-core items alone cannot occupy every CU
-  // (two workgroups per CU); otherwise the kernels just contend for CUs.
+  // Overlap only when the matrix-core items alone cannot occupy every CU (two four-wave
+  // workgroups or one eight-wave workgroup per CU); otherwise the kernels just contend for CUs.
   int matrix_items = 0;
   for (const Segment& s : plan.segments)
-    if (s.kernel == kMatrix) matrix_items += s.count;
+    if (s.kernel == kMatrix) matrix_items += s.count * ((s.param & kWideFlag) ? 2 : 1);
   // Single-stream mode (the flag, or a call that must allocate nothing, since the side stream is
   // created on first use) keeps every launch on the caller's stream.
   const bool single = (d->flags & PENSIEVE_FLAG_SINGLE_STREAM) || upload == Upload::kPageable;
@@ -853,7 +877,8 @@ pensieve_status run_plan(const pensieve_batch_desc* d, const Plan& plan, pk::Att
     const hipStream_t st = (fork && s.kernel == kVector) ? conc->side : stream;
     TraceScope trace(s.kernel == kMatrix ? kTraceMatrix : kTraceVector, s.count, st);
     if (s.kernel == kMatrix)
-      e = pk::launch_attn_mfma(a, d->dtype, d->kv_dtype, d->head_dim, s.param, st);
+      e = pk::launch_attn_mfma(a, d->dtype, d->kv_dtype, d->head_dim, s.param & (kWideFlag - 1),
+                               (s.param & kWideFlag) != 0, st);
     else
       e = pk::launch_attn_vector(a, d->dtype, d->kv_dtype, d->head_dim, s.param, st);
     if (e != hipSuccess) return hip_fail(e, s.kernel == kMatrix ? "matrix-core attention launch" : "vector attention launch");

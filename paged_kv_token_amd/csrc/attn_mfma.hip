@@ -4,13 +4,15 @@
 // Methodology: the kernel handles several input tokens over a cache that is
 // scattered or partly dropped and recomputed).
 //
-// Work item: up to 128 query vectors = (128 / G) consecutive rows of one
+// Work item: up to 32 NW query vectors = (32 NW / G) consecutive rows of one
 // request x the G query heads sharing KV head g, over one partition of the
-// request's KV blocks.  Four waves each own 32 query vectors (row-major over
-// (token, head)).  KV is streamed in 64-token tiles (four 16-token blocks
+// request's KV blocks.  NW = 4 or 8 waves each own 32 query vectors (row-major
+// over (token, head)).  KV is streamed in 64-token tiles (four 16-token blocks
 // found through the block table), each wave loading one block of every tile
-// straight into LDS one step ahead of its use, with one workgroup barrier per
-// tile.  Pools may hold f16 / bf16 or E4M3 codes (widened exactly on the way
+// (with eight waves, half of one) straight into LDS one step ahead of its use,
+// with one workgroup barrier per tile.  Four-wave workgroups run two to a CU;
+// an eight-wave workgroup fills a CU alone (its epilogue needs 135 KB of LDS at
+// d = 128) and feeds twice the query rows from each tile it loads.  Pools may hold f16 / bf16 or E4M3 codes (widened exactly on the way
 // from LDS to the MFMA operands).
 //
 // Per wave and tile, with v_mfma_f32_32x32x16_{f16,bf16}:
@@ -192,8 +194,8 @@ __device__ __forceinline__ int kswz8_rows(int t) {
   else return ((t >> 1) & 1) ^ ((t >> 2) & 1) ^ (((t >> 3) & 1) << 1);
 }
 
-template <int DT, int KVT, int D, int G>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
+template <int DT, int KVT, int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(const AttnArgs a) {
   using MM = Mfma<DT>;
   using vec8 = typename MM::vec8;
   constexpr bool F8 = KVT == kFP8;        // pools hold E4M3 codes, widened to DT in registers
@@ -209,16 +211,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   constexpr int KCH = KROW / 16;          // 16-byte chunks per K row
   constexpr int RPI = 1024 / KROW;        // K rows per DMA load
   static_assert(KVT == DT || F8, "stored K / V are the query type or E4M3 codes");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int NT = 64 * NW;             // threads of the workgroup
+  constexpr int NIW = NI * 4 / NW;        // 1 KB loads per wave, tensor and tile
   constexpr int OROW = D * 4 + 16;        // epilogue: fp32 output row
-  constexpr int OBYTES = 128 * OROW;
+  constexpr int OBYTES = 32 * NW * OROW;
   constexpr int PIPE = 4 * STAGE;         // K stages 0,1 then V stages 0,1
   constexpr int LDS_BYTES = PIPE > OBYTES ? PIPE : OBYTES;
   static_assert(G >= 1 && G <= 32 && (32 % G) == 0, "group size must divide 32");
-  static_assert(NI >= 1, "a block tile must fill whole 1 KB loads");
-  static_assert((KT * KCH) % 256 == 0, "the tail zeroing covers whole tiles");
+  static_assert(NIW >= 1 && NIW * NW == NI * 4, "a block tile must fill whole 1 KB loads of each wave");
+  static_assert((KT * KCH) % NT == 0, "the tail zeroing covers whole tiles");
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  __shared__ int s_wmax[4];
+  __shared__ int s_wmax[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -237,9 +242,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   const float slack_raw = kSlack / c;
 
   // ---- this lane's query row --------------------------------------------------------------
-  // Row block of this wave, rotated by the workgroup index: in items with fewer than 128 query
-  // vectors the busy waves then fall on different SIMDs in the two workgroups sharing a CU.
-  const int wr = (w + (int)(blockIdx.x & 3)) & 3;
+  // Row block of this wave, rotated by the workgroup index in four-wave workgroups: in items with
+  // fewer than 128 query vectors the busy waves then fall on different SIMDs in the two
+  // workgroups sharing a CU.
+  const int wr = NW == 4 ? (w + (int)(blockIdx.x & 3)) & 3 : w;
+  const int bw = w & 3;                   // block of each tile this wave loads
+  const int jw = (w >> 2) * NIW;          // its first 1 KB load of that block
   const int tok = wr * TOKW + n / G;
   const bool row_valid = tok < it.q_count;
   const size_t qrow = (size_t)row0 + it.q_begin + (row_valid ? tok : 0);
@@ -264,7 +272,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   const int pmin_w = uniform(wave_min_i(row_valid ? pos : INT_MAX));   // over valid rows only
   if (lane == 0) s_wmax[w] = pmax_w;
   __syncthreads();
-  const int pmax_wg = max(max(s_wmax[0], s_wmax[1]), max(s_wmax[2], s_wmax[3]));
+  int pmax_wg = s_wmax[0];
+#pragma unroll
+  for (int x = 1; x < NW; ++x) pmax_wg = max(pmax_wg, s_wmax[x]);
 
   // ---- key range of this item ----------------------------------------------------------------
   const int nblk = (L + 15) >> 4;
@@ -277,14 +287,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   const int ntiles = (t_end > t_begin) ? (t_end - t_begin + KT - 1) / KT : 0;
 
   // ---- LDS-DMA tile loads ---------------------------------------------------------------------
-  // Wave w loads block w of each tile, K and V, with NI buffer loads of 1 KB each straight into
-  // LDS (lane l lands at +16 l).  K stage: row t (0..63) at t * KROW, chunk c in slot
+  // Wave w loads block w % 4 of each tile, K and V, with NIW buffer loads of 1 KB each straight
+  // into LDS (lane l lands at +16 l): all NI loads of the block with four waves, loads
+  // jw .. jw + NIW - 1 of them with eight.  K stage: row t (0..63) at t * KROW, chunk c in slot
   // c ^ kswz(t).  V stage: the same rows, chunk c in slot c ^ vswz(t).  Source offsets inside a
   // block tile depend only on the lane: computed once.
-  uint32_t koff[NI], voff[NI];
+  uint32_t koff[NIW], voff[NIW];
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int t16 = j * RPI + lane / KCH;
+  for (int j = 0; j < NIW; ++j) {
+    const int t16 = (jw + j) * RPI + lane / KCH;
     const int ksw = F8 ? kswz8_rows<D>(t16) : kswz_rows<KCH>(t16);
     koff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ ksw) * 16);
     voff[j] = (uint32_t)(t16 * KROW + ((lane % KCH) ^ vswz_rows<D, F8>(t16)) * 16);
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // partition any block of it serves (those keys are masked).
   const int32_t* const bt_row = a.block_tables + (size_t)r * a.bt_stride;
   auto window_block = [&](int k) {            // this lane's block of window k
-    const int lb = kb0 + 4 * (64 * k + lane) + w;
+    const int lb = kb0 + 4 * (64 * k + lane) + bw;
     return bt_row[lb < kb1 ? lb : kb0];
   };
   int btw0 = 0, btw1 = 0;
@@ -311,15 +322,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   // When the request's rows fit one item, no other item reads this KV head's tiles of the
   // partition and the loads are non-temporal; otherwise the items of the request's other rows
   // read the same tiles at about the same time, through L2.
-  const bool read_once = uniform(q_r <= 4 * TOKW ? 1 : 0) != 0;
+  const bool read_once = uniform(q_r <= NW * TOKW ? 1 : 0) != 0;
   auto issue = [&](const uint8_t* pool, const uint32_t* offs, int tile, uint8_t* stage) {
     const uint8_t* src = pool + ((size_t)block_of(tile) * Hkv + g) * BLK;
     if (read_once) {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) lds_dma16<true>(src, BLK, offs[j], stage + w * BLK + j * 1024);
+      for (int j = 0; j < NIW; ++j) lds_dma16<true>(src, BLK, offs[j], stage + bw * BLK + (jw + j) * 1024);
     } else {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) lds_dma16<false>(src, BLK, offs[j], stage + w * BLK + j * 1024);
+      for (int j = 0; j < NIW; ++j) lds_dma16<false>(src, BLK, offs[j], stage + bw * BLK + (jw + j) * 1024);
     }
   };
   auto kstage = [&](int tile) { return lds + (tile & 1) * STAGE; };
@@ -428,8 +439,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
     issue(a.k_pool, koff, 0, kstage(0));
     if (ntiles > 1) issue(a.k_pool, koff, 1, kstage(1));
     issue(a.v_pool, voff, 0, vstage(0));
-    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NI>());
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<NI>());
+    if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NIW>());
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<NIW>());
     lds_barrier();
     if (!wave_idle) qk(lds, s_cur, nullptr);
   }
@@ -462,8 +473,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
       // Tail: keys at or past t_valid must contribute exactly 0; stale V may hold NaN, so their
       // whole rows are zeroed in LDS.
 #pragma unroll
-      for (int x = 0; x < KT * KCH / 256; ++x) {
-        const int ci = tid + 256 * x;        // (key row, chunk) pairs of the tile
+      for (int x = 0; x < KT * KCH / NT; ++x) {
+        const int ci = tid + NT * x;         // (key row, chunk) pairs of the tile
         const int row = ci / KCH, ch = ci % KCH;
         if (t0 + row >= t_valid) *reinterpret_cast<u32x4*>(v_cur + row * KROW + ch * 16) = u32x4{0u, 0u, 0u, 0u};
       }
@@ -617,8 +628,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   if (!split) {
     constexpr int CHR = D / 8;   // 8-element output chunks per row
 #pragma unroll
-    for (int x = 0; x < 128 * CHR / 256; ++x) {
-      const int ci = tid + 256 * x;
+    for (int x = 0; x < 32 * NW * CHR / NT; ++x) {
+      const int ci = tid + NT * x;
       const int rr = ci / CHR, cc = ci % CHR;
       const int otok = rr / G;
       if (otok >= it.q_count) continue;
@@ -634,8 +645,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   } else {
     constexpr int CHR = D / 4;   // 4-float chunks per row
 #pragma unroll
-    for (int x = 0; x < 128 * CHR / 256; ++x) {
-      const int ci = tid + 256 * x;
+    for (int x = 0; x < 32 * NW * CHR / NT; ++x) {
+      const int ci = tid + NT * x;
       const int rr = ci / CHR, cc = ci % CHR;
       const int otok = rr / G;
       if (otok >= it.q_count) continue;
@@ -646,35 +657,44 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(const AttnArgs a) {
   }
 }
 
-template <int DT, int KVT, int D>
+template <int DT, int KVT, int D, int NW>
 static hipError_t launch_mfma_d(const AttnArgs& args, int group, hipStream_t stream) {
-  dim3 grid(args.num_items), block(256);
+  dim3 grid(args.num_items), block(64 * NW);
   switch (group) {
-    case 1: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 1>), grid, block, stream, args); break;
-    case 2: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 2>), grid, block, stream, args); break;
-    case 4: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 4>), grid, block, stream, args); break;
-    case 8: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 8>), grid, block, stream, args); break;
-    case 16: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 16>), grid, block, stream, args); break;
-    case 32: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 32>), grid, block, stream, args); break;
+    case 1: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 1, NW>), grid, block, stream, args); break;
+    case 2: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 2, NW>), grid, block, stream, args); break;
+    case 4: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 4, NW>), grid, block, stream, args); break;
+    case 8: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 8, NW>), grid, block, stream, args); break;
+    case 16: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 16, NW>), grid, block, stream, args); break;
+    case 32: PK_LAUNCH((attn_mfma_kernel<DT, KVT, D, 32, NW>), grid, block, stream, args); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// Eight-wave workgroups exist for 2-byte pools only (an E4M3 block tile at d = 64 is a single
+// 1 KB load, which two waves cannot share).
 template <int DT, int KVT>
-static hipError_t launch_mfma_dt(const AttnArgs& args, int head_dim, int group, hipStream_t stream) {
-  return head_dim == 64 ? launch_mfma_d<DT, KVT, 64>(args, group, stream)
-                        : launch_mfma_d<DT, KVT, 128>(args, group, stream);
+static hipError_t launch_mfma_dt(const AttnArgs& args, int head_dim, int group, bool wide, hipStream_t stream) {
+  if constexpr (KVT == kFP8) {
+    if (wide) return hipErrorInvalidValue;
+  } else {
+    if (wide)
+      return head_dim == 64 ? launch_mfma_d<DT, KVT, 64, 8>(args, group, stream)
+                            : launch_mfma_d<DT, KVT, 128, 8>(args, group, stream);
+  }
+  return head_dim == 64 ? launch_mfma_d<DT, KVT, 64, 4>(args, group, stream)
+                        : launch_mfma_d<DT, KVT, 128, 4>(args, group, stream);
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group,
+hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group, bool wide,
                             hipStream_t stream) {
   if (args.num_items == 0) return hipSuccess;
   const bool f8 = kv_dtype == kFP8;
-  if (dtype == kF16) return f8 ? launch_mfma_dt<kF16, kFP8>(args, head_dim, group, stream)
-                               : launch_mfma_dt<kF16, kF16>(args, head_dim, group, stream);
-  if (dtype == kBF16) return f8 ? launch_mfma_dt<kBF16, kFP8>(args, head_dim, group, stream)
-                                : launch_mfma_dt<kBF16, kBF16>(args, head_dim, group, stream);
+  if (dtype == kF16) return f8 ? launch_mfma_dt<kF16, kFP8>(args, head_dim, group, wide, stream)
+                               : launch_mfma_dt<kF16, kF16>(args, head_dim, group, wide, stream);
+  if (dtype == kBF16) return f8 ? launch_mfma_dt<kBF16, kFP8>(args, head_dim, group, wide, stream)
+                                : launch_mfma_dt<kBF16, kBF16>(args, head_dim, group, wide, stream);
   return hipErrorInvalidValue;
 }
 

@@ -43,8 +43,9 @@ hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int kv_dtype, int
                               hipStream_t stream);
 
 // Matrix-core attention: items of up to 128 query vectors (tokens x the
-// whole head group), fp16/bf16 only.
-hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group,
+// whole head group) in four-wave workgroups, or with `wide` up to 256 in
+// eight-wave workgroups (2-byte pools only), fp16/bf16 queries.
+hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group, bool wide,
                             hipStream_t stream);
 
 // Copy n whole blocks (K and V runs of block_bytes each) from src to dst pools; pairs holds n

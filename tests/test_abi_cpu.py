@@ -391,3 +391,44 @@ def test_xcd_bins_keep_a_requests_items_together_inside_a_cost_class(lib):
                 assert key not in seen, f"bin {x}: items of {key} split into two runs"
                 seen.add(key)
             prev = key
+
+
+def _max_vectors(b, plan):
+    live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
+    G = b.num_heads // b.num_kv_heads
+    return int((live[:, 4] * G).max()) if len(live) else 0
+
+
+def test_eight_wave_items_only_where_four_wave_items_leave_the_gpu_short(lib):
+    """Matrix-core items of up to 256 query vectors (eight-wave workgroups) appear only in calls
+    whose 128-vector items would number fewer than 512 and that hold a request of more than 128
+    query vectors per KV head, with 2-byte pools; every other call keeps 128-vector items.  Rows
+    and partitions stay covered exactly once either way."""
+    lc = config_batch(4)                      # 512-row prefill: 320 four-wave items
+    plan = pk.pensieve_debug_plan(desc_for(lc))
+    assert _max_vectors(lc, plan) == 256
+    seen, want = _coverage(lc, plan)
+    assert np.array_equal(seen, want)
+    mat = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
+    assert len(mat) == 160                    # 2 row blocks x 40 heads x 2 partitions
+    # The explicit split pair: one partition leaves 160 four-wave items (eight-wave), 32 partitions
+    # 5120 (four-wave).
+    for P, widest in ((1, 256), (32, 128)):
+        plan_p = pk.pensieve_debug_plan(desc_for(lc), P)
+        assert _max_vectors(lc, plan_p) == widest
+        seen, want = _coverage(lc, plan_p, P)
+        assert np.array_equal(seen, want)
+    # The GQA recompute workload fills the GPU with four-wave items; the 13B batch has no request
+    # above 128 query vectors; E4M3 pools have no eight-wave kernel.
+    for b, over in ((config_batch(3), {}), (config_batch(1), {}), (lc, dict(kv_dtype=3, k_scale=1.0, v_scale=1.0))):
+        assert 0 < _max_vectors(b, pk.pensieve_debug_plan(desc_for(b, **over))) <= 128
+    # Groups of G query heads: rows of 256 / G tokens, the short request of the call too.
+    for hq, hkv in ((4, 4), (8, 4), (16, 4), (32, 4), (32, 1)):
+        b = custom_batch([3000, 700, 900], [300, 20, 1], num_heads=hq, num_kv_heads=hkv, head_dim=128,
+                         dtype="f16", seed=5)
+        plan = pk.pensieve_debug_plan(desc_for(b))
+        G = hq // hkv
+        live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
+        assert live[:, 4].max() == min(256 // G, 300)
+        seen, want = _coverage(b, plan)
+        assert np.array_equal(seen, want)

@@ -1,0 +1,76 @@
+"""Matrix-core items in eight-wave workgroups (256 query vectors, one workgroup per CU), against
+the CPU oracle.  The plan uses them in calls whose 128-vector items would not fill one round of
+the GPU and that hold a request of more than 128 query vectors per KV head: a long prefill or
+recompute request beside decode rows ("Stateful Large Language Model Serving with Pensieve",
+Methodology: prefill, recompute and decode rows of one step in one batch).  Each case covers
+head groups of 1-32, head_dim 64 and 128, f16 and bf16, recomputed leading rows, a short
+matrix-core request in the same launch (its items leave waves idle) and ragged row counts,
+through the default plan, the unsplit plan, one stream and the explicit split pair.
+"""
+
+import numpy as np
+import pytest
+
+import paged_kv_token_amd as pk
+from gpu_harness import run_attn, run_split, to_f64, upload
+from oracle_helpers import oracle_output, oracle_pools
+from workloads import custom_batch
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f16": 1e-2, "bf16": 1e-2}
+
+
+def _say(msg):
+    print(f"[wide] {msg}", flush=True)
+
+
+def _widest(gb, flags=0, P=0):
+    plan = pk.pensieve_debug_plan(gb.make_desc(flags), P)
+    live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
+    G = gb.batch.num_heads // gb.batch.num_kv_heads
+    return int((live[:, 4] * G).max()) if len(live) else 0
+
+
+CASES = [(1, 128, "bf16"), (1, 64, "f16"), (2, 128, "f16"), (4, 64, "bf16"), (8, 128, "bf16"),
+         (8, 64, "f16"), (16, 128, "f16"), (32, 128, "bf16"), (32, 64, "bf16")]
+
+
+@pytest.mark.parametrize("G,d,dtype", CASES)
+def test_eight_wave_items_match_the_oracle(G, d, dtype):
+    # Request 0: 64 recomputed rows + 237 new (ragged against 256 / G tokens per item); request 1:
+    # a short matrix-core request; 2: decode; 3: prefill with no history.
+    b = custom_batch([2500, 900, 1800, 0], [237, 20, 1, 40], [64, 0, 0, 0], num_heads=2 * G, num_kv_heads=2,
+                     head_dim=d, dtype=dtype, seed=400 + G + d)
+    ref = oracle_output(b, pools=oracle_pools(b))
+    gb = upload(b)
+    assert _widest(gb) > 128, "the plan should use eight-wave items"
+    outs = {
+        "default": lambda: run_attn(gb, 0),
+        "no_split": lambda: run_attn(gb, pk.PENSIEVE_FLAG_NO_SPLIT),
+        "single_stream": lambda: run_attn(gb, pk.PENSIEVE_FLAG_SINGLE_STREAM),
+        "split3": lambda: run_split(gb, 3)[3],
+    }
+    for name, fn in outs.items():
+        got = to_f64(fn())
+        assert np.all(np.isfinite(got)), name
+        err = float(np.max(np.abs(got - ref)))
+        _say(f"G={G} d={d} {dtype} {name}: max abs err {err:.3e}")
+        assert err <= TOL[dtype], (name, err)
+
+
+@pytest.mark.parametrize("G,dtype", [(1, "f16"), (8, "bf16")])
+def test_eight_wave_items_past_the_first_block_window(G, dtype):
+    """Unsplit items over 20 000 keys (313 tiles): each wave's block ids come from more than two
+    64-tile windows of its register-held block table, refilled as the item streams."""
+    b = custom_batch([20000, 3000], [300, 1], num_heads=2 * G, num_kv_heads=2, head_dim=128, dtype=dtype,
+                     seed=450 + G)
+    ref = oracle_output(b, pools=oracle_pools(b))
+    gb = upload(b)
+    assert _widest(gb, pk.PENSIEVE_FLAG_NO_SPLIT) > 128
+    got = to_f64(run_attn(gb, pk.PENSIEVE_FLAG_NO_SPLIT))
+    err = float(np.max(np.abs(got - ref)))
+    # Relative to the output's own scale too: at 20 000 keys |O| is small.
+    rel = err / float(np.max(np.abs(ref)))
+    _say(f"G={G} {dtype} unsplit 20k keys: max abs err {err:.3e} (relative {rel:.2e})")
+    assert err <= TOL[dtype] and rel <= 5e-2
