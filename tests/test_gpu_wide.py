@@ -5,14 +5,15 @@ recompute request beside decode rows ("Stateful Large Language Model Serving wit
 Methodology: prefill, recompute and decode rows of one step in one batch).  Each case covers
 head groups of 1-32, head_dim 64 and 128, f16 and bf16, recomputed leading rows, a short
 matrix-core request in the same launch (its items leave waves idle) and ragged row counts,
-through the default plan, the unsplit plan, one stream and the explicit split pair.
+through the default plan, the unsplit plan, one stream, the explicit split pair and the call that
+allocates nothing.
 """
 
 import numpy as np
 import pytest
 
 import paged_kv_token_amd as pk
-from gpu_harness import run_attn, run_split, to_f64, upload
+from gpu_harness import poison_, run_attn, run_split, to_f64, upload
 from oracle_helpers import oracle_output, oracle_pools
 from workloads import custom_batch
 
@@ -30,6 +31,16 @@ def _widest(gb, flags=0, P=0):
     live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
     G = gb.batch.num_heads // gb.batch.num_kv_heads
     return int((live[:, 4] * G).max()) if len(live) else 0
+
+
+def _noalloc(gb):
+    import torch
+    o = torch.empty_like(gb.q)
+    poison_(o, gb.batch.dtype)
+    pk.pensieve_attn_fwd_noalloc(gb.make_desc(0), gb.q, gb.k_pool, gb.v_pool, gb.block_tables, gb.context_lens,
+                                 gb.cu_q_lens, gb.q_pos, o)
+    torch.cuda.synchronize()
+    return o
 
 
 CASES = [(1, 128, "bf16"), (1, 64, "f16"), (2, 128, "f16"), (4, 64, "bf16"), (8, 128, "bf16"),
@@ -50,6 +61,7 @@ def test_eight_wave_items_match_the_oracle(G, d, dtype):
         "no_split": lambda: run_attn(gb, pk.PENSIEVE_FLAG_NO_SPLIT),
         "single_stream": lambda: run_attn(gb, pk.PENSIEVE_FLAG_SINGLE_STREAM),
         "split3": lambda: run_split(gb, 3)[3],
+        "noalloc": lambda: _noalloc(gb),
     }
     for name, fn in outs.items():
         got = to_f64(fn())
