@@ -60,6 +60,11 @@ def test_pools_beyond_4_gib():
     _say(f"pool {NUM_BLOCKS * block_bytes / 2**30:.2f} GiB per tensor; {far} of {len(used)} blocks past 4 GiB")
     assert NUM_BLOCKS * block_bytes > 2 ** 32 and far > len(used) // 2
     gb = upload(b)
+    # The 130-row request (260 query vectors per KV head) puts this small call on eight-wave
+    # matrix-core items, so their offsets past 4 GiB are checked too.
+    plan = pk.pensieve_debug_plan(gb.make_desc(0))
+    live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
+    assert int((live[:, 4] * (b.num_heads // b.num_kv_heads)).max()) == 256
     _check(b, to_f64(run_attn(gb, 0)), "default plan")
     _check(b, to_f64(run_attn(gb, pk.PENSIEVE_FLAG_VECTOR_ONLY)), "vector kernel")
     _check(b, to_f64(run_split(gb, 4)[3]), "split pair, 4 partitions")
