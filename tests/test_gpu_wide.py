@@ -86,3 +86,55 @@ def test_eight_wave_items_past_the_first_block_window(G, dtype):
     rel = err / float(np.max(np.abs(ref)))
     _say(f"G={G} {dtype} unsplit 20k keys: max abs err {err:.3e} (relative {rel:.2e})")
     assert err <= TOL[dtype] and rel <= 5e-2
+
+
+def _random_case(seed: int):
+    """Few KV heads, one request above 128 query vectors per KV head, up to four more (decode,
+    prefill, recompute), so the call usually takes eight-wave items; histories to 6 000 tokens."""
+    rng = np.random.default_rng(123000 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    hkv = int(rng.choice([1, 2]))
+    R = int(rng.integers(1, 6))
+    hist = rng.integers(0, 6000, size=R)
+    new = np.where(rng.random(R) < 0.5, 1, rng.integers(1, 400, size=R))
+    new[0] = int(rng.integers(max(1, 129 // G + 1), 600))
+    ev = np.array([16 * int(rng.integers(1, min(16, h // 32) + 1)) if h >= 32 and rng.random() < 0.3 else 0
+                   for h in hist])
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    b = custom_batch(hist, new, ev, num_heads=hkv * G, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                     seed=124000 + seed)
+    return b, int(rng.integers(2, 9))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_batches_through_eight_wave_items(seed):
+    b, P = _random_case(seed)
+    gb = upload(b)
+    widest = _widest(gb)
+    ref = oracle_output(b, pools=oracle_pools(b))
+    for name, fn in (("default", lambda: run_attn(gb, 0)), ("no_split", lambda: run_attn(gb, pk.PENSIEVE_FLAG_NO_SPLIT)),
+                     (f"split{P}", lambda: run_split(gb, P)[3])):
+        got = to_f64(fn())
+        assert np.all(np.isfinite(got)), name
+        err = float(np.max(np.abs(got - ref)))
+        _say(f"seed {seed} G={b.num_heads // b.num_kv_heads} d={b.head_dim} {b.dtype} q={b.q_lens.tolist()} "
+             f"widest item {widest} vectors, {name}: max abs err {err:.3e}")
+        assert err <= TOL[b.dtype], (seed, name, err)
+
+
+def test_random_batches_mostly_take_eight_wave_items():
+    """The seeded draws above exercise the eight-wave path: most of them plan 256-vector items
+    (checked on the host, no GPU work)."""
+    wide = 0
+    for seed in range(16):
+        b, _ = _random_case(seed)
+        desc = pk.make_desc(num_heads=b.num_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                            num_blocks=b.num_blocks, block_table_stride=b.block_table_stride,
+                            dtype={"f16": 1, "bf16": 2}[b.dtype], softmax_scale=b.softmax_scale,
+                            context_lens_host=b.context_lens, cu_q_lens_host=b.cu_q_lens,
+                            q_pos_host=None if b.has_default_positions else b.q_pos)
+        plan = pk.pensieve_debug_plan(desc)
+        live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
+        wide += int((live[:, 4] * (b.num_heads // b.num_kv_heads)).max()) > 128
+    assert wide >= 10, wide
