@@ -400,7 +400,8 @@ pensieve_status pensieve_attn_split_merge(const float* part_o, const float* part
  * item holds up to 128 query vectors (rows x heads), or up to 256 in calls
  * whose four-wave items would not fill one round of the GPU (about 512
  * items) and that hold a request of more than 128 query vectors per KV
- * head, with 2-byte pools: those run in eight-wave workgroups.
+ * head, with 2-byte pools or E4M3 pools at head_dim 128: those run in
+ * eight-wave workgroups.
  */
 pensieve_status pensieve_debug_plan(const pensieve_batch_desc* desc, int32_t num_partitions,
                                     int32_t* items_host, int32_t max_items, int32_t* num_items);

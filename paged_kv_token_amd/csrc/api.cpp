@@ -379,7 +379,7 @@ void build_plan(const pensieve_batch_desc* d, int num_partitions, Plan& plan) {
   std::stable_sort(reqs.begin(), reqs.end(),
                    [&](int a, int b) { return d->context_lens_host[a] > d->context_lens_host[b]; });
   bool wide = false;
-  if (mat && d->kv_dtype != PENSIEVE_FP8_E4M3) {
+  if (mat && (d->kv_dtype != PENSIEVE_FP8_E4M3 || d->head_dim == 128)) {   // kernels that exist
     long long narrow_items = 0;
     bool long_rows = false;
     for (int r : reqs) {

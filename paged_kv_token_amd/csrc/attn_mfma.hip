@@ -672,12 +672,12 @@ static hipError_t launch_mfma_d(const AttnArgs& args, int group, hipStream_t str
   return hipGetLastError();
 }
 
-// Eight-wave workgroups exist for 2-byte pools only (an E4M3 block tile at d = 64 is a single
-// 1 KB load, which two waves cannot share).
+// Eight-wave workgroups exist for 2-byte pools and for E4M3 pools at d = 128 (an E4M3 block
+// tile at d = 64 is a single 1 KB load, which two waves cannot share).
 template <int DT, int KVT>
 static hipError_t launch_mfma_dt(const AttnArgs& args, int head_dim, int group, bool wide, hipStream_t stream) {
   if constexpr (KVT == kFP8) {
-    if (wide) return hipErrorInvalidValue;
+    if (wide) return head_dim == 128 ? launch_mfma_d<DT, KVT, 128, 8>(args, group, stream) : hipErrorInvalidValue;
   } else {
     if (wide)
       return head_dim == 64 ? launch_mfma_d<DT, KVT, 64, 8>(args, group, stream)

@@ -44,7 +44,7 @@ hipError_t launch_attn_vector(const AttnArgs& args, int dtype, int kv_dtype, int
 
 // Matrix-core attention: items of up to 128 query vectors (tokens x the
 // whole head group) in four-wave workgroups, or with `wide` up to 256 in
-// eight-wave workgroups (2-byte pools only), fp16/bf16 queries.
+// eight-wave workgroups (2-byte pools, or E4M3 pools at head_dim 128), fp16/bf16 queries.
 hipError_t launch_attn_mfma(const AttnArgs& args, int dtype, int kv_dtype, int head_dim, int group, bool wide,
                             hipStream_t stream);
 

@@ -419,9 +419,14 @@ def test_eight_wave_items_only_where_four_wave_items_leave_the_gpu_short(lib):
         seen, want = _coverage(lc, plan_p, P)
         assert np.array_equal(seen, want)
     # The GQA recompute workload fills the GPU with four-wave items; the 13B batch has no request
-    # above 128 query vectors; E4M3 pools have no eight-wave kernel.
-    for b, over in ((config_batch(3), {}), (config_batch(1), {}), (lc, dict(kv_dtype=3, k_scale=1.0, v_scale=1.0))):
+    # above 128 query vectors; E4M3 pools have an eight-wave kernel at head_dim 128 only.
+    for b, over in ((config_batch(3), {}), (config_batch(1), {})):
         assert 0 < _max_vectors(b, pk.pensieve_debug_plan(desc_for(b, **over))) <= 128
+    f8 = dict(kv_dtype=3, k_scale=1.0, v_scale=1.0)
+    assert _max_vectors(lc, pk.pensieve_debug_plan(desc_for(lc, **f8))) == 256
+    lc64 = custom_batch([4000, 3000], [300, 1], num_heads=8, num_kv_heads=8, head_dim=64, dtype="bf16", seed=6)
+    assert _max_vectors(lc64, pk.pensieve_debug_plan(desc_for(lc64))) == 256
+    assert 0 < _max_vectors(lc64, pk.pensieve_debug_plan(desc_for(lc64, **f8))) <= 128
     # Groups of G query heads: rows of 256 / G tokens, the short request of the call too.
     for hq, hkv in ((4, 4), (8, 4), (16, 4), (32, 4), (32, 1)):
         b = custom_batch([3000, 700, 900], [300, 20, 1], num_heads=hq, num_kv_heads=hkv, head_dim=128,

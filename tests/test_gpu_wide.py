@@ -138,3 +138,24 @@ def test_random_batches_mostly_take_eight_wave_items():
         live = plan[(plan[:, 0] == 1) & (plan[:, 4] > 0)]
         wide += int((live[:, 4] * (b.num_heads // b.num_kv_heads)).max()) > 128
     assert wide >= 10, wide
+
+
+@pytest.mark.parametrize("G,dtype", [(1, "bf16"), (4, "f16"), (8, "bf16"), (32, "f16")])
+def test_eight_wave_items_on_e4m3_pools(G, dtype):
+    """E4M3 pools at head_dim 128 (each wave loads one 1 KB half of a 2 KB block): the codes
+    widen exactly, so the output matches the oracle over the same E4M3 pools at the gate
+    ("LLM上下文缓存与状态复用机制的分析和探索", section 4(3): the KV cache kept in 8-bit floats)."""
+    from oracle_helpers import fp8_kw
+    scales = (1 / 64, 1 / 48)
+    b = custom_batch([2500, 900, 1800, 0], [237, 20, 1, 40], [64, 0, 0, 0], num_heads=2 * G, num_kv_heads=2,
+                     head_dim=128, dtype=dtype, seed=470 + G)
+    ref = oracle_output(b, pools=oracle_pools(b, kv_fp8=scales), **fp8_kw(scales))
+    gb = upload(b, kv_fp8=scales)
+    assert _widest(gb) > 128, "the plan should use eight-wave items"
+    for name, fn in (("default", lambda: run_attn(gb, 0)), ("no_split", lambda: run_attn(gb, pk.PENSIEVE_FLAG_NO_SPLIT)),
+                     ("split3", lambda: run_split(gb, 3)[3])):
+        got = to_f64(fn())
+        assert np.all(np.isfinite(got)), name
+        err = float(np.max(np.abs(got - ref)))
+        _say(f"E4M3 G={G} {dtype} {name}: max abs err {err:.3e}")
+        assert err <= TOL[dtype], (name, err)
